@@ -1,0 +1,258 @@
+"""Thin ctypes binding over libmosaicq.so (declared in include/mosaicq.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  Torch tensors provide device memory and the current HIP stream.
+There is no fallback: if the library is missing or a call fails, an
+exception is raised.
+
+Function names follow the C ABI without the ``mq_`` prefix; the prefixed
+names are aliases.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmosaicq.so")
+
+GROUP = 128
+FLAG_DUMP_ACC = 1
+
+_c_i64 = ctypes.c_int64
+_c_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+
+_SIGS = {
+    "mq_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+    "mq_last_error": (ctypes.c_char_p, []),
+    "mq_version": (ctypes.c_int, []),
+    "mq_quantize_act": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "mq_select_blocks": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
+                                        _vp, _vp, _vp, _vp]),
+    "mq_pack_weights": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i32, _vp, _c_i32, _vp, _vp,
+                                       _vp, _vp, _vp, _vp, _vp]),
+    "mq_fused_gemm_workspace": (ctypes.c_int, [_c_i64, _c_i64, _c_i64,
+                                               ctypes.POINTER(ctypes.c_size_t)]),
+    "mq_fused_gemm": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i32,
+                                     _c_i32, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp,
+                                     ctypes.c_size_t, ctypes.c_uint32, _vp, _vp]),
+    "mq_validate_csr": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i32, _c_i32, _vp]),
+}
+
+_lib = None
+
+
+class MosaicQError(RuntimeError):
+    def __init__(self, fn: str, status: int, detail: str):
+        super().__init__(f"{fn} failed: {status_str(status)} ({status}): {detail}")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmosaicq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -m dense_sparse_w4a4_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_str(s: int) -> str:
+    return lib().mq_status_str(int(s)).decode()
+
+
+def last_error() -> str:
+    return lib().mq_last_error().decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MosaicQError(fn, status, last_error())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+# ----------------------------------------------------------------------------
+# Entry points
+# ----------------------------------------------------------------------------
+
+def quantize_act(x: torch.Tensor, qa: Optional[torch.Tensor] = None,
+                 sa: Optional[torch.Tensor] = None, stream=None):
+    """x fp16 [M, K] (row stride % 8 == 0) -> (qa uint8 [M, K/2], sa fp32 [M, K/128])."""
+    _dev(x, torch.float16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be 2-D with unit column stride")
+    M, K = x.shape
+    if qa is None:
+        qa = torch.empty((M, K // 2), dtype=torch.uint8, device=x.device)
+    if sa is None:
+        sa = torch.empty((M, max(K // GROUP, 0)), dtype=torch.float32, device=x.device)
+    _check("mq_quantize_act", lib().mq_quantize_act(
+        _ptr(x), M, K, x.stride(0), _ptr(qa), _ptr(sa), _stream(stream)))
+    return qa, sa
+
+
+def select_blocks(w: torch.Tensor, x_calib: torch.Tensor, block: int, n_select: int,
+                  stream=None):
+    """Delta-score top-K.  Returns (selected int32 [n_select] ascending,
+    delta fp64 [B], hdiag fp64 [K])."""
+    _dev(w, torch.float16, "w")
+    _dev(x_calib, torch.float16, "x_calib")
+    w = w.contiguous()
+    x_calib = x_calib.contiguous()
+    N, K = w.shape
+    T = x_calib.shape[0]
+    if x_calib.shape[1] != K:
+        raise ValueError("x_calib must have K columns")
+    B = (N // block) * (K // block) if block else 0
+    sel = torch.empty(max(n_select, 0), dtype=torch.int32, device=w.device)
+    delta = torch.empty(max(B, 1), dtype=torch.float64, device=w.device)
+    H = torch.empty(K, dtype=torch.float64, device=w.device)
+    _check("mq_select_blocks", lib().mq_select_blocks(
+        _ptr(w), _ptr(x_calib) if T else None, N, K, T, block, n_select,
+        _ptr(sel) if n_select else None, _ptr(delta), _ptr(H), _stream(stream)))
+    return sel, delta[:B], H
+
+
+@dataclass
+class PackedLayer:
+    """Packed dense base + CSR residual (device tensors), as mq_pack_weights writes it."""
+    N: int
+    K: int
+    block: int
+    qw: torch.Tensor       # uint8 [N, K/2]
+    sw: torch.Tensor       # fp16  [N, K/128]
+    row_ptr: torch.Tensor  # int32 [N/b + 1]
+    col_idx: torch.Tensor  # int32 [n_select]
+    qr: torch.Tensor       # uint8 [n_select, b, b/2]
+    sr: torch.Tensor       # fp16  [n_select, b]
+
+    @property
+    def n_select(self) -> int:
+        return int(self.col_idx.numel())
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.qw, self.sw, self.row_ptr, self.col_idx, self.qr, self.sr))
+
+    def clone(self) -> "PackedLayer":
+        return PackedLayer(self.N, self.K, self.block, self.qw.clone(), self.sw.clone(),
+                           self.row_ptr.clone(), self.col_idx.clone(), self.qr.clone(),
+                           self.sr.clone())
+
+
+def pack_weights(w: torch.Tensor, block: int, selected: torch.Tensor, stream=None) -> PackedLayer:
+    """w fp16 [N, K] + ascending selected block ids -> PackedLayer."""
+    _dev(w, torch.float16, "w")
+    _dev(selected, torch.int32, "selected")
+    w = w.contiguous()
+    selected = selected.contiguous()
+    N, K = w.shape
+    ns = int(selected.numel())
+    dev = w.device
+    b = int(block)
+    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    sw = torch.empty((N, K // GROUP), dtype=torch.float16, device=dev)
+    row_ptr = torch.empty(N // b + 1 if b else 1, dtype=torch.int32, device=dev)
+    col_idx = torch.empty(ns, dtype=torch.int32, device=dev)
+    qr = torch.empty((ns, b, b // 2), dtype=torch.uint8, device=dev)
+    sr = torch.empty((ns, b), dtype=torch.float16, device=dev)
+    _check("mq_pack_weights", lib().mq_pack_weights(
+        _ptr(w), N, K, b, _ptr(selected) if ns else None, ns, _ptr(qw), _ptr(sw),
+        _ptr(row_ptr), _ptr(col_idx) if ns else None, _ptr(qr) if ns else None,
+        _ptr(sr) if ns else None, _stream(stream)))
+    return PackedLayer(N, K, b, qw, sw, row_ptr, col_idx, qr, sr)
+
+
+def fused_gemm_workspace(M: int, N: int, K: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mq_fused_gemm_workspace", lib().mq_fused_gemm_workspace(M, N, K, ctypes.byref(n)))
+    return int(n.value)
+
+
+def fused_gemm(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer,
+               out: Optional[torch.Tensor] = None, dump: bool = False,
+               workspace: Optional[torch.Tensor] = None, stream=None):
+    """Y fp16 [M, N] = deq(Qa(X) Q(W)^T) + deq(Qa(X) R^T).
+
+    With dump=True also returns the exact accumulators
+    (acc_base int32 [M, N, K/128], acc_res int32 [n_select, M, b])."""
+    _dev(qa, torch.uint8, "qa")
+    _dev(sa, torch.float32, "sa")
+    M = qa.shape[0]
+    N, K, b, ns = layer.N, layer.K, layer.block, layer.n_select
+    if qa.shape[1] * 2 != K or not qa.is_contiguous() or not sa.is_contiguous():
+        raise ValueError("qa/sa must be contiguous and match the layer's K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=qa.device)
+    _dev(out, torch.float16, "out")
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != M or out.shape[1] != N:
+        raise ValueError("out must be [M, N] with unit column stride")
+    wsb = fused_gemm_workspace(M, N, K)
+    if wsb and (workspace is None or workspace.numel() * workspace.element_size() < wsb):
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=qa.device)
+    G = K // GROUP
+    acc = None
+    if dump:
+        acc = torch.empty(M * N * G + ns * M * b, dtype=torch.int32, device=qa.device)
+    _check("mq_fused_gemm", lib().mq_fused_gemm(
+        _ptr(qa), _ptr(sa), M, N, K, _ptr(layer.qw), _ptr(layer.sw), b, ns,
+        _ptr(layer.row_ptr) if ns else None, _ptr(layer.col_idx) if ns else None,
+        _ptr(layer.qr) if ns else None, _ptr(layer.sr) if ns else None,
+        _ptr(out), out.stride(0), _ptr(workspace) if wsb else None, wsb,
+        FLAG_DUMP_ACC if dump else 0, _ptr(acc), _stream(stream)))
+    if dump:
+        base = acc[: M * N * G].view(M, N, G)
+        res = acc[M * N * G:].view(ns, M, b)
+        return out, base, res
+    return out
+
+
+def validate_csr(layer: PackedLayer, stream=None) -> None:
+    ns = layer.n_select
+    _check("mq_validate_csr", lib().mq_validate_csr(
+        _ptr(layer.row_ptr), _ptr(layer.col_idx) if ns else None, layer.N, layer.K,
+        layer.block, ns, _stream(stream)))
+
+
+def layer_forward(x: torch.Tensor, layer: PackedLayer, out: Optional[torch.Tensor] = None,
+                  stream=None) -> torch.Tensor:
+    """The online hot path: Qa(X) then the fused GEMM (two launches)."""
+    qa, sa = quantize_act(x, stream=stream)
+    return fused_gemm(qa, sa, layer, out=out, stream=stream)
+
+
+mq_quantize_act = quantize_act
+mq_select_blocks = select_blocks
+mq_pack_weights = pack_weights
+mq_fused_gemm = fused_gemm
+mq_fused_gemm_workspace = fused_gemm_workspace
+mq_validate_csr = validate_csr

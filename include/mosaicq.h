@@ -1,0 +1,196 @@
+/*
+ * mosaicq.h - C ABI of the MI355X (gfx950) MosaicQuant fused linear layer.
+ *
+ * The layer computes Y = deq(Qa(X) . Q(W)^T) + deq(Qa(X) . R^T): a dense
+ * 4-bit base Q(W) of the whole weight plus a 4-bit residual R kept only on
+ * the b x b weight blocks with the largest Hessian-guided Delta-scores.
+ *   - decomposition W ~ Q(W) + R, both parts 4-bit: MosaicQuant technical
+ *     summary, gist.science/pt/paper/2606.15652, Metodologia 1;
+ *   - block-level budget, Delta-score, top-K: same page, Metodologia 2;
+ *   - one fused kernel for quantisation, dense compute, sparse compensation
+ *     and reduce-sum: same page, Metodologia 3 (ZipperEngine), and the
+ *     authors' abstract, fugumt.com/fugumt/paper_check/2606.15652v1.
+ *
+ * Fixed configuration: groups of 128 input channels; symmetric 4-bit codes
+ * in [-7, 7] (code = clamp(rint(v / s), -7, 7), 0 when s == 0, the quotient
+ * an IEEE fp32 division rounded half-to-even); scale = amax / 7 in fp32,
+ * rounded to fp16 (nearest-even, subnormals kept) for weights and residuals
+ * and kept fp32 for activations; residual block edge b in {32, 64, 128}.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked "host".  Matrices are
+ *     row-major.  fp16 data is passed as uint16_t bit patterns.
+ *   - 4-bit codes are packed two per byte along the input-channel axis,
+ *     two's complement: byte i = (q[2i] & 0xF) | ((q[2i+1] & 0xF) << 4).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Work is enqueued on it and the call returns without synchronising;
+ *     the caller keeps every buffer alive until the stream has drained.
+ *   - The caller owns and allocates every buffer.  The library keeps no
+ *     pointer after a call returns and allocates no device memory.
+ *   - Every argument is validated before anything is enqueued.  On a
+ *     violation nothing is enqueued, the first violation's code is returned
+ *     and mq_last_error() describes it.  A failed launch returns
+ *     MQ_ERR_HIP.  Faults inside kernels surface at the caller's next
+ *     synchronisation.  No call aborts or throws.
+ *   - Device pointers must be 16-byte aligned; leading dimensions are in
+ *     elements.
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified codes.
+ */
+#ifndef MOSAICQ_H
+#define MOSAICQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MQ_OK = 0,
+  MQ_ERR_NULL_PTR = 1,   /* a required pointer is NULL                        */
+  MQ_ERR_SHAPE = 2,      /* a size is negative, not a multiple it must be, or
+                            a leading dimension is too small                   */
+  MQ_ERR_ALIGN = 3,      /* a pointer or leading dimension is misaligned       */
+  MQ_ERR_BLOCK = 4,      /* residual block edge not in {32, 64, 128}           */
+  MQ_ERR_BUDGET = 5,     /* n_select outside [0, number of blocks]             */
+  MQ_ERR_CSR = 6,        /* CSR arrays inconsistent (mq_validate_csr only)     */
+  MQ_ERR_WORKSPACE = 7,  /* workspace too small                                */
+  MQ_ERR_HIP = 8,        /* the HIP runtime reported an error                  */
+  MQ_ERR_ARG = 9         /* any other invalid argument (unknown flag, ...)     */
+} mq_status;
+
+/* Human-readable name of a status code (static string). */
+const char* mq_status_str(int status);
+
+/* Detail of the most recent failure on the calling thread ("" if none).
+   The string stays valid until the next mq_* call on that thread. */
+const char* mq_last_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int mq_version(void);
+
+/* Group of input channels sharing one scale. */
+#define MQ_GROUP 128
+
+/*
+ * Activation quantisation Qa(X): per token m and group j of 128 channels,
+ *   sa[m][j] = max_k |x[m][k]| / 7         (fp32 division, kept fp32)
+ *   qa code  = clamp(rint(x / sa[m][j]), -7, 7)   (0 if sa == 0).
+ * [summary-pt Metodologia 3: quantisation is one stage of the fused
+ * pipeline; Resultados: W4A4.]
+ *   x  : fp16 [M][ldx], ldx >= K, ldx % 8 == 0
+ *   qa : uint8 [M][K/2] packed codes (output)
+ *   sa : fp32  [M][K/128] (output)
+ *   M >= 0 (M == 0 enqueues nothing), K > 0, K % 128 == 0.
+ */
+mq_status mq_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                          uint8_t* qa, float* sa, void* stream);
+
+/*
+ * Offline block selection.  For W fp16 [N][K] and calibration tokens
+ * Xc fp16 [T][K]:
+ *   base   sw = f16(amax/7) per (row, group), qw = clamp(rint(W/sw))
+ *   error  E = W - sw*qw (fp32)
+ *   per b x b block i and block row r: sr = f16(max_c |E| / 7),
+ *          R_hat = sr * clamp(rint(E / sr))
+ *   H[k]   = sum_t Xc[t][k]^2 in fp64, t = 0, 1, ... in order
+ *   Delta_i = sum_r ( sum_c H[k] * (E^2 - (E - R_hat)^2) ) in fp64, each sum
+ *            left to right from +0, k = kt*b + c
+ *   selected = the n_select ids with the largest Delta (ties: lower id),
+ *              written in ascending id order; id = nt*(K/b) + kt.
+ * [summary-pt Metodologia 2: Hessian-guided Delta-score weighting the
+ * residual error by the input channels' diagonal Hessian; top-K blocks.]
+ *   w        : fp16 [N][K];  x_calib: fp16 [T][K]
+ *   N % block == 0, K % 128 == 0, T >= 0, block in {32, 64, 128},
+ *   0 <= n_select <= (N/block)*(K/block), (N/block)*(K/block) < 2^31
+ *   selected : int32 [n_select] (output; may be NULL when n_select == 0)
+ *   delta_out: fp64 [(N/block)*(K/block)] (output, required: also used as
+ *              the scores' working storage)
+ *   hdiag_out: fp64 [K] (output, required)
+ */
+mq_status mq_select_blocks(const uint16_t* w, const uint16_t* x_calib,
+                           int64_t N, int64_t K, int64_t T, int32_t block,
+                           int32_t n_select, int32_t* selected,
+                           double* delta_out, double* hdiag_out, void* stream);
+
+/*
+ * Pack the dense 4-bit base and the residual of the selected blocks.
+ * [summary-pt Metodologia 1: W ~ Q(W) + R, both 4-bit.]
+ *   w        : fp16 [N][K]
+ *   selected : int32 [n_select], strictly ascending block ids in range
+ *              (as written by mq_select_blocks); other contents give
+ *              unspecified residual output but every access stays in bounds
+ *   qw       : uint8 [N][K/2]       packed base codes (output)
+ *   sw       : fp16  [N][K/128]     base scales (output)
+ *   row_ptr  : int32 [N/block + 1]  CSR by output tile row (output)
+ *   col_idx  : int32 [n_select]     block column kt, ascending per row (output)
+ *   qr       : uint8 [n_select][block][block/2]  residual codes; row r is
+ *              output channel nt*block + r, column c input kt*block + c
+ *   sr       : fp16  [n_select][block]  residual scale per block row (output)
+ */
+mq_status mq_pack_weights(const uint16_t* w, int64_t N, int64_t K, int32_t block,
+                          const int32_t* selected, int32_t n_select,
+                          uint8_t* qw, uint16_t* sw, int32_t* row_ptr,
+                          int32_t* col_idx, uint8_t* qr, uint16_t* sr,
+                          void* stream);
+
+/* Debug flag for mq_fused_gemm: also store the exact integer accumulators. */
+#define MQ_FLAG_DUMP_ACC 1u
+
+/*
+ * Bytes of workspace mq_fused_gemm needs for this shape (host output).
+ * The current kernels need none; the call exists so callers can size a
+ * buffer once and stay compatible with split-K schedules.
+ */
+mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes);
+
+/*
+ * The fused layer (ZipperEngine), one kernel:
+ *   acc_base[m][n][j] = sum_{k in group j} qa[m][k] * qw[n][k]        (int32, exact)
+ *   acc_res[i][m][r]  = sum_{c<b} qa[m][kt_i*b + c] * qr_i[r][c]      (int32, exact)
+ *   y[m][n] = f16( sum_j sa[m][j]*sw[n][j]*acc_base[m][n][j]
+ *                + sum_{i in tile row n/b} sa[m][j_i]*sr_i[n - nt*b]*acc_res[i][m][n - nt*b] )
+ * with the scale products and the sum in fp32, j_i = kt_i*b/128.  Each
+ * residual block reuses the activation tile already staged for the dense
+ * base in the same K step.
+ * [summary-pt Metodologia 3; abstract: sparse block computation fused into
+ * the dense 4-bit GEMM.]
+ *   qa, sa   : as written by mq_quantize_act for M x K
+ *   qw, sw   : as written by mq_pack_weights for N x K
+ *   block, n_select, row_ptr, col_idx, qr, sr: the residual, as written by
+ *              mq_pack_weights; n_select == 0 gives the dense-only layer
+ *              (row_ptr, col_idx, qr, sr may then be NULL).  A CSR that
+ *              points outside [0, n_select) or past K is clipped, never
+ *              read out of bounds (check it with mq_validate_csr).
+ *   y        : fp16 [M][ldy], ldy >= N, ldy % 8 == 0 (output)
+ *   workspace: may be NULL when mq_fused_gemm_workspace reports 0
+ *   flags    : 0 or MQ_FLAG_DUMP_ACC
+ *   acc_dump : with MQ_FLAG_DUMP_ACC, int32 [M*N*(K/128) + n_select*M*block]:
+ *              acc_base as [M][N][K/128] followed by acc_res as
+ *              [n_select][M][block]; otherwise ignored (may be NULL)
+ *   M >= 0 (M == 0 enqueues nothing), N % block == 0, K % 128 == 0.
+ */
+mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N, int64_t K,
+                        const uint8_t* qw, const uint16_t* sw,
+                        int32_t block, int32_t n_select, const int32_t* row_ptr,
+                        const int32_t* col_idx, const uint8_t* qr, const uint16_t* sr,
+                        uint16_t* y, int64_t ldy,
+                        void* workspace, size_t workspace_bytes,
+                        uint32_t flags, int32_t* acc_dump, void* stream);
+
+/*
+ * Synchronous CSR check (copies row_ptr and col_idx to the host and waits
+ * for `stream`): row_ptr[0] == 0, non-decreasing, row_ptr[N/block] ==
+ * n_select, col_idx strictly ascending within a row and < K/block.
+ * Returns MQ_OK or MQ_ERR_CSR.
+ */
+mq_status mq_validate_csr(const int32_t* row_ptr, const int32_t* col_idx,
+                          int64_t N, int64_t K, int32_t block, int32_t n_select,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOSAICQ_H */

@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/mosaicq.h declares, and rejects invalid arguments with the documented
+status codes before touching the device (fake, never-dereferenced pointer
+values are used where a pointer must be non-NULL)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from dense_sparse_w4a4_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mosaicq.h")
+
+OK, NULLP, SHAPE, ALIGN, BLOCK, BUDGET, CSR, WS, HIP, ARG = range(10)
+
+P = ctypes.c_void_p(0x1000)      # aligned fake device address (never reached)
+PMIS = ctypes.c_void_p(0x1008)   # misaligned by 8
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(ops.LIB_PATH):
+        from dense_sparse_w4a4_amd import build
+        build.build(verbose=False)
+    return ops.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mq_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(L):
+    syms = declared_symbols()
+    assert {"mq_quantize_act", "mq_select_blocks", "mq_pack_weights", "mq_fused_gemm"} <= set(syms)
+    for s in syms:
+        assert hasattr(L, s), f"{s} not exported"
+
+
+def test_status_strings_and_version(L):
+    assert ops.status_str(0) == "MQ_OK"
+    assert ops.status_str(SHAPE) == "MQ_ERR_SHAPE"
+    assert ops.status_str(99) == "MQ_ERR_UNKNOWN"
+    assert L.mq_version() >> 16 == 1
+
+
+def test_quantize_act_validation(L):
+    f = L.mq_quantize_act
+    assert f(P, 4, 100, 128, P, P, None) == SHAPE            # K % 128
+    assert f(P, -1, 128, 128, P, P, None) == SHAPE           # M < 0
+    assert f(P, 4, 128, 64, P, P, None) == SHAPE             # ldx < K
+    assert f(None, 4, 128, 128, P, P, None) == NULLP
+    assert f(P, 4, 128, 132, P, P, None) == ALIGN            # ldx % 8
+    assert f(PMIS, 4, 128, 128, P, P, None) == ALIGN
+    assert "128" in ops.last_error() or "align" in ops.last_error()
+    assert f(None, 0, 128, 128, None, None, None) == OK      # M == 0: nothing to do
+
+
+def test_select_validation(L):
+    f = L.mq_select_blocks
+    assert f(P, P, 512, 512, 64, 48, 6, P, P, P, None) == BLOCK
+    assert f(P, P, 500, 512, 64, 64, 6, P, P, P, None) == SHAPE
+    assert f(P, P, 512, 500, 64, 64, 6, P, P, P, None) == SHAPE
+    assert f(P, P, 512, 512, 64, 64, 65, P, P, P, None) == BUDGET
+    assert f(P, P, 512, 512, 64, 64, -1, P, P, P, None) == BUDGET
+    assert f(P, P, 512, 512, 64, 64, 6, None, P, P, None) == NULLP
+    assert f(P, None, 512, 512, 64, 64, 6, P, P, P, None) == NULLP
+    assert f(P, P, 512, 512, 64, 64, 6, P, None, P, None) == NULLP
+    assert f(P, P, 512, 512, 64, 64, 6, P, P, PMIS, None) == ALIGN
+
+
+def test_pack_validation(L):
+    f = L.mq_pack_weights
+    args = dict(w=P, N=512, K=512, b=64, sel=P, ns=6, qw=P, sw=P, rp=P, ci=P, qr=P, sr=P)
+
+    def call(**kw):
+        a = {**args, **kw}
+        return f(a["w"], a["N"], a["K"], a["b"], a["sel"], a["ns"], a["qw"], a["sw"], a["rp"],
+                 a["ci"], a["qr"], a["sr"], None)
+    assert call(b=16) == BLOCK
+    assert call(N=96) == SHAPE
+    assert call(K=192) == SHAPE
+    assert call(ns=65) == BUDGET
+    assert call(qr=None) == NULLP
+    assert call(rp=None) == NULLP
+    assert call(sw=PMIS) == ALIGN
+
+
+def _gemm(L, **kw):
+    a = dict(qa=P, sa=P, M=16, N=512, K=512, qw=P, sw=P, b=64, ns=6, rp=P, ci=P, qr=P, sr=P,
+             y=P, ldy=512, ws=None, wsb=0, flags=0, dump=None)
+    a.update(kw)
+    return L.mq_fused_gemm(a["qa"], a["sa"], a["M"], a["N"], a["K"], a["qw"], a["sw"], a["b"],
+                           a["ns"], a["rp"], a["ci"], a["qr"], a["sr"], a["y"], a["ldy"], a["ws"],
+                           a["wsb"], a["flags"], a["dump"], None)
+
+
+def test_fused_gemm_validation(L):
+    assert _gemm(L, flags=4) == ARG
+    assert _gemm(L, b=100) == BLOCK
+    assert _gemm(L, M=-3) == SHAPE
+    assert _gemm(L, N=100) == SHAPE
+    assert _gemm(L, K=640 - 64) == SHAPE
+    assert _gemm(L, ldy=256) == SHAPE
+    assert _gemm(L, ns=65) == BUDGET
+    assert _gemm(L, qa=None) == NULLP
+    assert _gemm(L, ci=None) == NULLP
+    assert _gemm(L, flags=1) == NULLP                 # dump without a buffer
+    assert _gemm(L, ldy=516) == ALIGN
+    assert _gemm(L, qw=PMIS) == ALIGN
+    assert _gemm(L, M=0, qa=None, y=None) == OK      # empty batch
+
+
+def test_workspace_query(L):
+    n = ctypes.c_size_t(123)
+    assert L.mq_fused_gemm_workspace(16, 4096, 4096, ctypes.byref(n)) == OK
+    assert n.value == 0
+    assert L.mq_fused_gemm_workspace(16, 4096, 4096, None) == NULLP
+
+
+def test_validate_csr_argument_errors(L):
+    f = L.mq_validate_csr
+    assert f(P, P, 512, 512, 48, 6, None) == BLOCK
+    assert f(None, P, 512, 512, 64, 6, None) == NULLP
+    assert f(P, None, 512, 512, 64, 6, None) == NULLP
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(ops, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(ops, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        ops.lib()

@@ -1,0 +1,209 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact: activation codes and scales, H, Delta, selected ids, packed base
+and residual bytes and scales, the int32 accumulators (debug dump).
+Within tolerance (parity_util.YTOL): the fp16 output y.
+Full-size layer shapes check every integer/byte output in full and y on
+sampled block-row tiles the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from dense_sparse_w4a4_amd import ops
+from dense_sparse_w4a4_amd import synthetic as syn
+from parity_util import (assert_packed_equal, assert_y_close, dev, f16_bits, host,
+                         tile_rows_reference)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _check_act(x16: np.ndarray, ldx_pad: int = 0):
+    M, K = x16.shape
+    if ldx_pad:
+        big = np.zeros((M, K + ldx_pad), np.float16)
+        big[:, :K] = x16
+        xt = dev(big)[:, :K]
+    else:
+        xt = dev(x16)
+    qa, sa = ops.quantize_act(xt)
+    rq, rs = oracle.quantize_act(x16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(qa), oracle.pack_nibbles(rq))
+    assert np.array_equal(host(sa).view(np.uint32), rs.view(np.uint32))
+
+
+@pytest.mark.parametrize("M,K,pad", [(1, 128, 0), (5, 512, 8), (16, 4096, 0), (17, 14336, 0),
+                                     (300, 1024, 64)])
+def test_act_quant_bit_exact(M, K, pad):
+    spec = syn.LayerSpec("t", K=K, N=128)
+    _check_act(syn.make_acts(spec, M, seed=M), pad)
+
+
+def test_act_quant_special_values():
+    rng = np.random.default_rng(0)
+    x = np.zeros((6, 256), np.float16)
+    x[0, :] = 0                                                    # all-zero groups
+    x[1, :] = (rng.standard_normal(256) * 1e-6).astype(np.float16)  # subnormals
+    x[2, :] = np.float16(65504.0) * np.sign(rng.standard_normal(256)).astype(np.float16)
+    x[3, :128] = np.arange(128) * 0.5 - 32                         # ties at amax 32 -> s = 32/7
+    x[4, :128] = 7.0 * (np.arange(128) % 3 - 1)
+    x[4, 128:] = np.linspace(-3.5, 3.5, 128)
+    x[5, :] = np.float16(6e-8)
+    _check_act(x)
+
+
+def _layer(spec, seed=0):
+    return syn.make_weight(spec, seed), syn.make_calib(spec, seed)
+
+
+@pytest.mark.parametrize("b", [32, 64, 128])
+def test_select_bit_exact_tiny(b):
+    spec = syn.TINY.with_block(b)
+    w, xc = _layer(spec)
+    sel, delta, H = ops.select_blocks(dev(w), dev(xc), b, spec.n_select)
+    rsel, rdelta, rH = oracle.select_blocks(w, xc, b, spec.n_select)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(H).view(np.uint64), rH.view(np.uint64))
+    assert np.array_equal(host(delta).view(np.uint64), rdelta.view(np.uint64))
+    assert np.array_equal(host(sel), rsel)
+
+
+def test_select_ties_and_extremes():
+    # integer weights with a 7 in every group: E = 0, every score is 0, ties
+    # must resolve to the lowest ids; also n_select = 0 and n_select = B
+    rng = np.random.default_rng(1)
+    w = rng.integers(-7, 8, size=(128, 256)).astype(np.float16)
+    w[:, ::128] = 7
+    xc = rng.standard_normal((16, 256)).astype(np.float16)
+    for ns in (0, 3, 8):
+        sel, delta, _ = ops.select_blocks(dev(w), dev(xc), 64, ns)
+        torch.cuda.synchronize()
+        assert host(sel).tolist() == list(range(ns))
+        assert not np.any(host(delta))
+    spec = syn.TINY
+    w, xc = _layer(spec, seed=3)
+    sel, _, _ = ops.select_blocks(dev(w), dev(xc), 64, spec.n_blocks)
+    torch.cuda.synchronize()
+    assert host(sel).tolist() == list(range(spec.n_blocks))
+
+
+@pytest.mark.parametrize("b,rho", [(32, 0.1), (64, 0.0), (64, 0.1), (64, 1.0), (128, 0.2)])
+def test_pack_bit_exact(b, rho):
+    spec = syn.TINY.with_block(b, rho)
+    w, xc = _layer(spec, seed=b)
+    rsel, _, _ = oracle.select_blocks(w, xc, b, spec.n_select)
+    layer = ops.pack_weights(dev(w), b, dev(rsel.astype(np.int32)))
+    ref = oracle.pack_weights(w, b, rsel)
+    torch.cuda.synchronize()
+    assert_packed_equal(layer, ref)
+    ops.validate_csr(layer)
+
+
+GEMM_CASES = [
+    # M, N, K, b, rho
+    (16, 512, 512, 64, 0.10),
+    (1, 512, 512, 64, 0.10),
+    (17, 256, 384, 32, 0.25),
+    (40, 384, 256, 128, 0.50),
+    (3, 128, 128, 64, 1.00),
+    (16, 512, 512, 64, 0.0),
+    (70, 256, 1024, 64, 0.10),
+    (2, 64, 2048, 32, 0.05),
+]
+
+
+@pytest.mark.parametrize("M,N,K,b,rho", GEMM_CASES)
+def test_fused_gemm_accumulators_exact_and_y(M, N, K, b, rho):
+    spec = syn.LayerSpec("g", K=K, N=N, w_outlier_frac=0.01, x_outlier_count=3,
+                         T=32, block=b, rho=rho)
+    w, xc = _layer(spec, seed=M + N)
+    x = syn.make_acts(spec, M, seed=K)
+    rsel, _, _ = oracle.select_blocks(w, xc, b, spec.n_select)
+    ref = oracle.pack_weights(w, b, rsel)
+    rqa, rsa = oracle.quantize_act(x)
+    y_ref, acc_ref, res_ref = oracle.fused_gemm(rqa, rsa, ref)
+    # the GPU GEMM consumes the oracle's packed data (inputs, not expected values)
+    layer = ops.PackedLayer(N, K, b, dev(ref["qw"]), dev(ref["sw"]), dev(ref["row_ptr"]),
+                            dev(ref["col_idx"]), dev(ref["qr"]), dev(ref["sr"]))
+    qa, sa = dev(oracle.pack_nibbles(rqa)), dev(rsa)
+    y, acc, res = ops.fused_gemm(qa, sa, layer, dump=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc).astype(np.int64), acc_ref)
+    if len(res_ref):
+        assert np.array_equal(host(res).astype(np.int64), np.stack(res_ref))
+    assert_y_close(y, y_ref)
+    # the production launch (no dump) gives the same bits
+    y2 = ops.fused_gemm(qa, sa, layer)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y2).view(np.uint16), host(y).view(np.uint16))
+
+
+def test_end_to_end_tiny_and_determinism():
+    spec = syn.TINY
+    x = syn.make_acts(spec, syn.TINY_M)
+    w, xc = _layer(spec)
+    ref = oracle.layer_reference(x, w, xc, spec.block, spec.n_select)
+    sel, _, _ = ops.select_blocks(dev(w), dev(xc), spec.block, spec.n_select)
+    layer = ops.pack_weights(dev(w), spec.block, sel)
+    xt = dev(x)
+    y = ops.layer_forward(xt, layer)
+    y_again = ops.layer_forward(xt, layer)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sel), ref["selected"])
+    assert_packed_equal(layer, ref["packed"])
+    assert_y_close(y, ref["y"])
+    assert np.array_equal(host(y).view(np.uint16), host(y_again).view(np.uint16))
+
+
+def test_empty_batch_is_a_no_op():
+    spec = syn.TINY
+    w, xc = _layer(spec)
+    layer = ops.pack_weights(dev(w), 64, torch.zeros(0, dtype=torch.int32, device="cuda"))
+    x = torch.zeros((0, 512), dtype=torch.float16, device="cuda")
+    y = ops.layer_forward(x, layer)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 512)
+
+
+FULL = [(K, N, M) for (K, N) in syn.LLAMA3_8B_SHAPES for M in (1, 16, 2048)]
+
+
+@pytest.mark.parametrize("K,N,M", FULL)
+def test_full_size_llama3_8b(K, N, M):
+    spec = syn.llama3_8b(K, N)
+    w, xc = _layer(spec)
+    x = syn.make_acts(spec, M)
+    wt = dev(w)
+    sel, delta, H = ops.select_blocks(wt, dev(xc), spec.block, spec.n_select)
+    layer = ops.pack_weights(wt, spec.block, sel)
+    qa, sa = ops.quantize_act(dev(x))
+    y = ops.fused_gemm(qa, sa, layer)
+    torch.cuda.synchronize()
+    # integer/byte outputs in full
+    rqa, rsa = oracle.quantize_act(x)
+    assert np.array_equal(host(qa), oracle.pack_nibbles(rqa))
+    assert np.array_equal(host(sa).view(np.uint32), rsa.view(np.uint32))
+    rsel, rdelta, rH = oracle.select_blocks(w, xc, spec.block, spec.n_select)
+    assert np.array_equal(host(H).view(np.uint64), rH.view(np.uint64))
+    assert np.array_equal(host(delta).view(np.uint64), rdelta.view(np.uint64))
+    assert np.array_equal(host(sel), rsel)
+    ref = oracle.pack_weights(w, spec.block, rsel)
+    assert_packed_equal(layer, ref)
+    # y on sampled block-row tiles (includes the tiles with the most residual blocks)
+    counts = np.diff(ref["row_ptr"])
+    NT = N // spec.block
+    tiles = sorted({0, NT - 1, int(np.argmax(counts)), NT // 2})
+    yt = host(y)
+    for nt, yref in tile_rows_reference(rqa, rsa, ref, tiles).items():
+        assert_y_close(torch.from_numpy(yt[:, nt * 64:(nt + 1) * 64]), yref)
