@@ -1,0 +1,290 @@
+"""Throughput of the fused W4A4 + block-sparse INT4 residual layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the online hot path - activation quantisation then
+the fused GEMM - for every (shape, M) of the workload, with inputs resident
+in HBM.  The offline part (Delta-score selection and packing) runs once on
+the GPU before timing.  Every (shape, M) in a step reads its own copy of the
+packed weights, and whole copies of the step's data rotate between steps so
+the footprint is >= 512 MB: the 256 MB Infinity Cache cannot serve weights
+from a previous launch.
+
+Printed JSON (one line on stdout):
+  value      algorithmic bytes of the step / step time (GB/s), both kernels
+  tops       algorithmic integer ops of the step / step time
+  roofline   the fused GEMM (dominant kernel): algorithmic bytes (decode) or
+             ops (prefill) per launch / average launch time from HIP events
+             recorded around each launch on the launch stream
+  cpu_baseline  the CPU oracle (quantise + fused GEMM) on a bounded sample
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused W4A4+10% residual GEMM TOPS & HBM GB/s vs roofline, M=1..4096"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
+ROTATE_BYTES = 512 << 20
+
+
+def workload(name: str):
+    from dense_sparse_w4a4_amd import synthetic as syn
+    if name == "llama3-8b-decode":
+        return [(syn.llama3_8b(K, N), syn.LLAMA3_8B_DECODE_M) for (K, N) in syn.LLAMA3_8B_SHAPES], "hbm"
+    if name == "llama3-8b-prefill":
+        return [(syn.llama3_8b(K, N), [syn.LLAMA3_8B_PREFILL_M]) for (K, N) in syn.LLAMA3_8B_SHAPES], "mfma"
+    if name.startswith("qwen3-32b"):
+        ms = {"qwen3-32b-decode": [1, 16], "qwen3-32b-256": [256], "qwen3-32b-4096": [4096]}.get(name)
+        if ms is None:
+            raise SystemExit(f"unknown workload {name}")
+        return [(syn.qwen3_32b(K, N), ms) for (K, N) in syn.QWEN3_32B_SHAPES], ("hbm" if max(ms) <= 16 else "mfma")
+    if name.startswith("llama3-70b"):
+        # llama3-70b-b{32,64,128}-r{0,5,10,20}
+        parts = name.split("-")
+        b = int(parts[2][1:])
+        rho = int(parts[3][1:]) / 100.0
+        return [(syn.llama3_70b(b, rho), [syn.LLAMA3_70B_M])], "mfma"
+    if name == "tiny":
+        return [(syn.TINY, [syn.TINY_M])], "hbm"
+    raise SystemExit(f"unknown workload {name}")
+
+
+def gemm_bytes(M, N, K, b, ns):
+    """Compulsory bytes of one fused GEMM call (each byte counted once)."""
+    G = K // 128
+    return (N * K // 2 + 2 * N * G + ns * (b * b // 2 + 2 * b) + 4 * ns + 4 * (N // b + 1)
+            + M * K // 2 + 4 * M * G + 2 * M * N)
+
+
+def act_bytes(M, K):
+    return 2 * M * K + M * K // 2 + 4 * M * (K // 128)
+
+
+def gemm_ops(M, N, K, b, ns):
+    return 2 * M * N * K + 2 * M * ns * b * b
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "dense_sparse_w4a4_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(wname: str):
+    """HBM bytes per GEMM launch measured with rocprofv3 counters, if the
+    stored measurement was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{wname}.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("sources_sha") != kernel_sources_sha():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(layers, budget_s: float):
+    """Time the oracle's online path on a bounded sample of the workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    from dense_sparse_w4a4_amd import synthetic as syn
+    done, tbytes, tops, tsec = [], 0, 0, 0.0
+    wall0 = time.perf_counter()
+    for spec, ms in layers:
+        w = syn.make_weight(spec)
+        xc = syn.make_calib(spec)
+        sel, _, _ = oracle.select_blocks(w, xc, spec.block, spec.n_select)
+        packed = oracle.pack_weights(w, spec.block, sel)
+        for M in ms:
+            x = syn.make_acts(spec, M)
+            t0 = time.perf_counter()
+            qa, sa = oracle.quantize_act(x)
+            oracle.fused_gemm(qa, sa, packed)
+            dt = time.perf_counter() - t0
+            tsec += dt
+            tbytes += act_bytes(M, spec.K) + gemm_bytes(M, spec.N, spec.K, spec.block, len(sel))
+            tops += gemm_ops(M, spec.N, spec.K, spec.block, len(sel))
+            done.append(f"{spec.K}x{spec.N}@M={M}")
+            if tsec >= budget_s:
+                break
+        if tsec >= budget_s or time.perf_counter() - wall0 > 4 * budget_s:
+            break
+    return dict(value=tbytes / tsec / 1e9, unit="GB/s", tops=tops / tsec / 1e12, cores=int(threads),
+                kind="oracle", seconds=round(tsec, 3),
+                sample="oracle quantize_act + fused_gemm (numpy, fp64 scales) on " + ", ".join(done))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama3-8b-decode")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer shards by output channels with no exchange; see the sharding "
+              "design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dense_sparse_w4a4_amd import ops
+    from dense_sparse_w4a4_amd import synthetic as syn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    ops.lib()
+    layers, bound = workload(args.workload)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+
+    # ---- offline: select + pack once per shape (GPU), then replicate ----
+    t0 = time.perf_counter()
+    base = []
+    for spec, ms in layers:
+        wt = torch.from_numpy(syn.make_weight(spec)).to(dev)
+        xct = torch.from_numpy(syn.make_calib(spec)).to(dev)
+        sel, _, _ = ops.select_blocks(wt, xct, spec.block, spec.n_select)
+        layer = ops.pack_weights(wt, spec.block, sel)
+        xs = {M: torch.from_numpy(syn.make_acts(spec, M)).to(dev) for M in ms}
+        base.append((spec, ms, layer, xs))
+        del wt, xct
+    torch.cuda.synchronize()
+    pairs = [(spec, M) for spec, ms, _, _ in base for M in ms]
+    step_footprint = sum(layer.nbytes() + 2 * xs[M].numel() for spec, ms, layer, xs in base for M in ms)
+    R = max(1, -(-ROTATE_BYTES // step_footprint))
+    sets = []
+    for r in range(R):
+        s = []
+        for spec, ms, layer, xs in base:
+            for M in ms:
+                L = layer.clone()
+                x = xs[M].clone()
+                qa = torch.empty((M, spec.K // 2), dtype=torch.uint8, device=dev)
+                sa = torch.empty((M, spec.K // 128), dtype=torch.float32, device=dev)
+                y = torch.empty((M, spec.N), dtype=torch.float16, device=dev)
+                s.append((spec, M, L, x, qa, sa, y))
+        sets.append(s)
+    torch.cuda.synchronize()
+    log(f"[bench] workload {args.workload}: {len(pairs)} (shape, M) pairs per step, "
+        f"{R} rotating copies x {step_footprint / 2**20:.1f} MiB, setup {time.perf_counter() - t0:.1f}s")
+
+    per_step_bytes = sum(act_bytes(M, s.K) + gemm_bytes(M, s.N, s.K, s.block, s.n_select) for s, M in pairs)
+    per_step_gemm_bytes = sum(gemm_bytes(M, s.N, s.K, s.block, s.n_select) for s, M in pairs)
+    per_step_ops = sum(gemm_ops(M, s.N, s.K, s.block, s.n_select) for s, M in pairs)
+
+    def step(i, events=None):
+        for p, (spec, M, L, x, qa, sa, y) in enumerate(sets[i % R]):
+            ops.quantize_act(x, qa, sa)
+            if events is not None:
+                events[p][0].record()
+            ops.fused_gemm(qa, sa, L, out=y)
+            if events is not None:
+                events[p][1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, HIP events around every fused GEMM launch ----
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in pairs] for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(i, evs[i])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall
+    total_ms = max(start.elapsed_time(end), wall * 1e3)
+    ms_per_step = total_ms / args.steps
+    gemm_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in evs])  # [steps, pairs]
+    mean_gemm_ms = gemm_ms.mean(axis=0)
+
+    for p, (spec, M) in enumerate(pairs):
+        gb = gemm_bytes(M, spec.N, spec.K, spec.block, spec.n_select)
+        go = gemm_ops(M, spec.N, spec.K, spec.block, spec.n_select)
+        t = mean_gemm_ms[p] * 1e-3
+        log(f"[bench]   K={spec.K:6d} N={spec.N:6d} M={M:5d}: gemm {t * 1e6:8.2f} us  "
+            f"{gb / t / 1e9:8.1f} GB/s ({gb / t / 1e9 / HBM_PEAK_GBS:5.1%} HBM)  "
+            f"{go / t / 1e12:8.2f} TOPS ({go / t / 1e12 / INT8_MFMA_PEAK_TOPS:5.1%} int8 MFMA)")
+
+    launches = len(pairs)
+    gemm_time_s = float(mean_gemm_ms.sum()) * 1e-3
+    if bound == "hbm":
+        achieved = per_step_gemm_bytes / gemm_time_s / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(achieved / HBM_PEAK_GBS, 4))
+    else:
+        achieved = per_step_ops / gemm_time_s / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_MFMA_PEAK_TOPS,
+                    unit="TOP/s", frac=round(achieved / INT8_MFMA_PEAK_TOPS, 4))
+    roof["traffic"] = traffic_from_profile(args.workload)
+    roof["kernel"] = "gemm_skinny_kernel"
+    roof["avg_launch_us"] = round(gemm_time_s / launches * 1e6, 3)
+    roof["alg_bytes_per_launch"] = per_step_gemm_bytes / launches
+    roof["alg_ops_per_launch"] = per_step_ops / launches
+
+    if args.copy_calibration:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": METRIC,
+        "value": round(per_step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "tops": round(per_step_ops / (ms_per_step * 1e-3) / 1e12, 3),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": args.workload,
+            "shapes_KxN": [[s.K, s.N] for s, _, _, _ in base],
+            "M": sorted({M for _, M in pairs}),
+            "group": 128, "block": base[0][0].block, "rho": base[0][0].rho,
+            "codes": "w4a4 int4 symmetric, int8 MFMA, int32 accumulators, fp32 epilogue, fp16 out",
+            "bytes_per_step": per_step_bytes, "ops_per_step": per_step_ops,
+            "rotating_copies": R,
+        },
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
