@@ -47,407 +47,307 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* p) {
 
 constexpr float kInv256 = 1.0f / 256.0f;
 
-// Skinny tile: 16 output channels x (16*MT) tokens per workgroup.  The KS
-// waves split the K groups into contiguous runs and their partial sums are
-// reduced through LDS in wave order.  Activations are the MFMA A operand
-// (rows = tokens), weights the B operand (columns = channels): lane l holds
-// channel n0 + l%16 and tokens 4*(l/16) + i of each 16-token tile.
+// Streaming tile for small M: 16 output channels x 16 tokens per workgroup
+// (grid.y walks 16-token tiles).  The KS waves of a workgroup split the K
+// groups into contiguous runs; partial sums are reduced through LDS in wave
+// order.  Activations are the MFMA A operand (rows = tokens), weights the B
+// operand (columns = channels): lane l owns channel n0 + l%16 and tokens
+// 4*(l/16) + i.
 //
-// Memory pipeline per wave (all loads are unconditional so the hardware
-// counters never wait on a load that is not needed yet):
-//   * dense fragments (weights + activations) of batch t+1 (U groups) are
-//     issued before batch t is computed (register double buffer);
-//   * the tile row's CSR entries sit in a register window (lane l holds the
-//     block column of entry wbase + l), so locating a batch's residual blocks
-//     is a ballot, not a chain of dependent loads;
-//   * up to RB residual blocks of batch t are fetched right after batch t's
-//     dense MFMAs and consumed one batch later, together with the activation
-//     fragments of batch t that are kept for that purpose (the zipper reuses
-//     them instead of reloading activations); any further blocks of the batch
-//     are loaded and consumed at once.
-// Scales are staged in LDS once per workgroup (activation scales transposed
-// to [group][token] and pre-multiplied by 1/256).
-template <int BLK, int KS, int MT, int U, bool DUMP>
-__global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(GemmArgs a) {
-  constexpr int RB = 4;
-  constexpr int TM = 16 * MT;
+// Each wave consumes one stream of items: first its dense groups, then the
+// residual blocks of its tile row whose block column lies in its groups,
+// then padding.  Every item, dense or residual, is the same work - one
+// 16-byte B fragment (weight or residual codes), one 16-byte A fragment
+// (the activation codes of the item's group), one 2-byte scale (sw[n][j] or
+// sr[e][r]), two MFMAs and a scale-and-add - so the zipper is literally the
+// same instruction stream applied to the residual, against the activation
+// codes of the same group.  Items are processed in units of U, and the next
+// unit's loads are in flight while the current unit computes.  Because every
+// unit issues exactly the same loads (padding items read a cached valid
+// address and are masked to zero), the hardware load counters are waited on
+// exactly, and nothing in the loop depends on the CSR lookup, which is read
+// from a register window only when the stream reaches its residual items.
+template <int BLK, int KS, int U, bool DUMP>
+__global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = (int)(a.K / kGroup);
-  const int KT = (int)(a.K / BLK);
-  float* sa_t = reinterpret_cast<float*>(smem);                            // [G][TM]
-  uint16_t* sw_t = reinterpret_cast<uint16_t*>(smem + (size_t)G * TM * 4);  // [G][16]
-  int* csr_l = reinterpret_cast<int*>(smem + (size_t)G * TM * 4 + (size_t)G * 32);  // [<= KT]
-  float* red = reinterpret_cast<float*>(smem);                             // [KS][TM][17]
+  float* sa_t = reinterpret_cast<float*>(smem);  // [G][16]: sa/256 of the tile's tokens
+  float* red = reinterpret_cast<float*>(smem);   // [KS][16][17] after the stream
 
   // readfirstlane tells the compiler the wave index is uniform, so loop
-  // bounds and guards below stay scalar branches (no exec-masked loads)
+  // bounds and item metadata stay scalar
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int ch = lane >> 4;
   const int64_t n0 = (int64_t)blockIdx.x * 16;
-  const int64_t m0 = (int64_t)blockIdx.y * TM;
+  const int64_t m0 = (int64_t)blockIdx.y * 16;
   const int64_t Kh = a.K / 2;
   const int gb = wave * G / KS;
-  const int ge = (wave + 1) * G / KS;
-  const int nb = (ge - gb + U - 1) / U;
+  const int ng = (wave + 1) * G / KS - gb;
 
-  const uint8_t* wp = a.qw + (n0 + r16) * Kh + ch * 16;
-  // Token rows past M read row M-1 instead (their results are never stored).
-  const uint8_t* xp[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int64_t m = m0 + t * 16 + r16;
-    xp[t] = a.qa + (m < a.M ? m : a.M - 1) * Kh + ch * 16;
-  }
+  const uint8_t* wrow = a.qw + (n0 + r16) * Kh + ch * 16;
+  // token rows past M read row M-1 (computed, never stored)
+  const int64_t mr = m0 + r16;
+  const uint8_t* xrow = a.qa + (mr < a.M ? mr : a.M - 1) * Kh + ch * 16;
+  const uint16_t* swrow = a.sw + (n0 + r16) * G;
 
-  // This tile's rows lie in block row nt, block rows rrow .. rrow+15.
+  // Residual CSR row of this tile (block row nt, block rows rrow .. rrow+15).
+  // Lane l of the window holds the block column of entry wbase + l.
   const int nt = (int)(n0 / BLK);
   const int rrow = (int)(n0 - (int64_t)nt * BLK);
   int rp0 = 0, rp1 = 0;
   if (a.n_select > 0) {
-    rp0 = min(max(a.row_ptr[nt], 0), a.n_select);
-    rp1 = min(max(a.row_ptr[nt + 1], rp0), a.n_select);
+    rp0 = a.row_ptr[nt];
+    rp1 = a.row_ptr[nt + 1];
   }
-  const bool has_res = rp1 > rp0;
+  int wbase = 0;
+  int kt_win = 0;
 
-  struct Dense {
-    uint4 W[U];
-    uint4 X[MT][U];
+  struct Unit {
+    uint4 A[U];     // B-operand fragments (weights or residual codes)
+    uint4 X[U];     // A-operand fragments (activation codes)
+    uint32_t S[U];  // scale bits (fp16 in the low half)
+    float4 sa[U];   // activation scales of the lane's 4 tokens (from LDS)
   };
-  struct Slots {
-    uint4 R[RB];
-    uint32_t M[RB];  // all-ones where the lane's chunk lies inside the block
-    uint16_t S[RB];  // residual scale bits (converted where used)
-    int e[RB], j[RB];
-    int n;
+  struct Meta {
+    int j[U];       // group of the item (for the activation scale)
+    int e[U];       // residual entry, or -1 for a dense item, -2 for padding
+    uint32_t rm[U]; // lane mask for the B fragment
   };
 
-  auto fetch_dense = [&](Dense& D, int jb) {
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int j = min(jb + u, ge - 1);
-      D.W[u] = ld16(wp + (int64_t)j * 64);
-#pragma unroll
-      for (int t = 0; t < MT; ++t) D.X[t][u] = ld16(xp[t] + (int64_t)j * 64);
+  // ---- the wave's residual items: [e_first, e_first + nr) ----
+  // Register work only (the window was loaded once in the prologue), so no
+  // load in the stream depends on it.  Entries the single window cannot
+  // show run after the stream (see below).
+  int nr = -1, e_first = rp0;
+  bool window_full = false;
+  auto ensure_nr = [&]() {
+    if (nr >= 0) return;
+    nr = 0;
+    if (rp1 <= rp0 || ng <= 0) return;
+    const int kt0 = gb * kGroup / BLK;
+    const int kt1 = (gb + ng) * kGroup / BLK;
+    const bool valid = wbase + lane < rp1;
+    const int below = __popcll(__ballot(valid && kt_win < kt0));
+    const int inside = __popcll(__ballot(valid && kt_win >= kt0 && kt_win < kt1));
+    e_first = wbase + below;
+    nr = inside;
+    window_full = (below + inside == 64) && (wbase + 64 < rp1);
+  };
+
+  auto item_meta = [&](int i, Meta& M, int u, const uint8_t*& ap, const uint16_t*& sp) {
+    if (i < ng) {
+      const int j = gb + i;
+      M.j[u] = j;
+      M.e[u] = -1;
+      M.rm[u] = 0xFFFFFFFFu;
+      ap = wrow + (int64_t)j * 64;
+      sp = swrow + j;
+    } else if (i < ng + nr) {
+      const int e = e_first + (i - ng);
+      const int kt = __builtin_amdgcn_readlane(kt_win, e - wbase);
+      const int j = kt * BLK / kGroup;
+      const int lo = kt * BLK - j * kGroup;
+      const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK);
+      M.j[u] = j;
+      M.e[u] = e;
+      M.rm[u] = act ? 0xFFFFFFFFu : 0u;
+      ap = a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + r16) * (BLK / 2) + (act ? 16 * ch - lo / 2 : 0);
+      sp = a.sr + (int64_t)e * BLK + rrow + r16;
+    } else {
+      M.j[u] = gb;
+      M.e[u] = -2;
+      M.rm[u] = 0u;
+      ap = wrow;
+      sp = swrow;
     }
   };
 
-  float y[MT][4];
+  // issue the U items of unit t (exactly 3U loads, always)
+  auto fetch = [&](Unit& D, Meta& M, int t) {
+    if ((t + 1) * U > ng) ensure_nr();
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
+    for (int u = 0; u < U; ++u) {
+      const uint8_t* ap;
+      const uint16_t* sp;
+      item_meta(t * U + u, M, u, ap, sp);
+      D.A[u] = ld16(ap);
+      D.X[u] = ld16(xrow + (int64_t)M.j[u] * 64);
+      D.S[u] = *sp;
+    }
+  };
+  // activation scales of a unit, read from LDS one unit ahead of use
+  auto fetch_sa = [&](Unit& D, const Meta& M) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) y[t][i] = 0.f;
+    for (int u = 0; u < U; ++u)
+      D.sa[u] = *reinterpret_cast<const float4*>(sa_t + M.j[u] * 16 + 4 * ch);
+  };
+
+  float y[4] = {0.f, 0.f, 0.f, 0.f};
   const v4i zero = {0, 0, 0, 0};
 
-  auto load_sa4 = [&](int j, float (&sa4)[MT][4]) {
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      const float4 s4 = *reinterpret_cast<const float4*>(sa_t + j * TM + t * 16 + 4 * ch);
-      sa4[t][0] = s4.x;
-      sa4[t][1] = s4.y;
-      sa4[t][2] = s4.z;
-      sa4[t][3] = s4.w;
-    }
-  };
-
-  auto residual = [&](uint4 R, uint32_t rm, float srf, int e, int j, const uint4 (&Xg)[MT]) {
-    float sa4[MT][4];
-    load_sa4(j, sa4);
-    const v4i Rlo = widen8(R.x & rm, R.y & rm);
-    const v4i Rhi = widen8(R.z & rm, R.w & rm);
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      v4i racc = mfma(widen8(Xg[t].x, Xg[t].y), Rlo, zero);
-      racc = mfma(widen8(Xg[t].z, Xg[t].w), Rhi, racc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) y[t][i] = fmaf(sa4[t][i] * srf, (float)racc[i], y[t][i]);
-      if (DUMP) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t m = m0 + t * 16 + 4 * ch + i;
-          if (m < a.M)
-            a.acc_dump[a.M * a.N * G + ((int64_t)e * a.M + m) * BLK + rrow + r16] = racc[i] >> 8;
-        }
-      }
-    }
-  };
-
-  // residual block against the activation fragments of group u of a batch
-  // (u is uniform; the unrolled select keeps register indices static)
-  auto residual_in = [&](const uint4 (&X)[MT][U], int u, uint4 R, uint32_t rm, float srf, int e,
-                         int j) {
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      if (uu == u) {
-        uint4 Xg[MT];
-#pragma unroll
-        for (int tt = 0; tt < MT; ++tt) Xg[tt] = X[tt][uu];
-        residual(R, rm, srf, e, j, Xg);
-      }
-    }
-  };
-
-  auto res_ptr = [&](int e, int kt, uint32_t& rm) {
-    const int js = kt * BLK / kGroup;
-    const int lo = kt * BLK - js * kGroup;
-    const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK);
-    rm = act ? 0xFFFFFFFFu : 0u;
-    return a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + r16) * (BLK / 2) +
-           (act ? 16 * ch - lo / 2 : 0);
-  };
-
-  auto compute_dense = [&](const Dense& D, int jb) {
+  auto compute = [&](const Unit& D, const Meta& M) {
+    const float4* sa4 = D.sa;
+    v4i acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int j = jb + u;
-      if (j >= ge) break;
-      float sa4[MT][4];
-      load_sa4(j, sa4);
-      const float swf = h2f(sw_t[j * 16 + r16]);
-      const v4i Wlo = widen8(D.W[u].x, D.W[u].y);
-      const v4i Whi = widen8(D.W[u].z, D.W[u].w);
+      const uint32_t rm = M.rm[u];
+      acc[u] = mfma(widen8(D.X[u].x, D.X[u].y), widen8(D.A[u].x & rm, D.A[u].y & rm), zero);
+      acc[u] = mfma(widen8(D.X[u].z, D.X[u].w), widen8(D.A[u].z & rm, D.A[u].w & rm), acc[u]);
+    }
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        v4i acc = mfma(widen8(D.X[t][u].x, D.X[t][u].y), Wlo, zero);
-        acc = mfma(widen8(D.X[t][u].z, D.X[t][u].w), Whi, acc);
+    for (int u = 0; u < U; ++u) {
+      const float sc = (M.e[u] == -2) ? 0.f : h2f((uint16_t)D.S[u]);
+      y[0] = fmaf(sa4[u].x * sc, (float)acc[u][0], y[0]);
+      y[1] = fmaf(sa4[u].y * sc, (float)acc[u][1], y[1]);
+      y[2] = fmaf(sa4[u].z * sc, (float)acc[u][2], y[2]);
+      y[3] = fmaf(sa4[u].w * sc, (float)acc[u][3], y[3]);
+      if (DUMP && M.e[u] != -2) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) y[t][i] = fmaf(sa4[t][i] * swf, (float)acc[i], y[t][i]);
-        if (DUMP) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t m = m0 + t * 16 + 4 * ch + i;
-            if (m < a.M) a.acc_dump[(m * a.N + n0 + r16) * G + j] = acc[i] >> 8;
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = m0 + 4 * ch + i;
+          if (m < a.M) {
+            if (M.e[u] == -1)
+              a.acc_dump[(m * a.N + n0 + r16) * G + M.j[u]] = acc[u][i] >> 8;
+            else
+              a.acc_dump[a.M * a.N * G + ((int64_t)M.e[u] * a.M + m) * BLK + rrow + r16] =
+                  acc[u][i] >> 8;
           }
         }
       }
     }
   };
 
-  // ---- prologue: batch 0, scale staging loads, CSR window ----
-  Dense cur, nxt;
-  if (nb > 0) fetch_dense(cur, gb);
-
-  const int bd = 64 * KS;
-  const int na = TM * G, nw = 16 * G;
-  float sav[4];
-  uint16_t swv[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int ia = min((int)threadIdx.x + q * bd, na - 1);
-    const int ma = ia / G;
-    sav[q] = a.sa[(m0 + ma < a.M ? m0 + ma : a.M - 1) * G + (ia - ma * G)];
-    const int iw = min((int)threadIdx.x + q * bd, nw - 1);
-    swv[q] = a.sw[(n0 + iw / G) * G + (iw - (iw / G) * G)];
+  // ---- prologue: unit 0 in flight, then the activation scales to LDS ----
+  Unit U0, U1;
+  Meta M0, M1;
+  // unit 0 holds only dense items unless the wave has fewer than U groups;
+  // in that case the CSR lookup happens first
+  if (ng > 0 && ng >= U) fetch(U0, M0, 0);
+  if (a.n_select > 0) {
+    rp0 = min(max(rp0, 0), a.n_select);
+    rp1 = min(max(rp1, rp0), a.n_select);
+    wbase = rp0;
+    if (rp1 > rp0) kt_win = a.col_idx[min(rp0 + lane, rp1 - 1)];
   }
-
-  // the tile row's CSR entries (block columns) are copied to LDS, so the
-  // residual bookkeeping in the loop never waits on global memory
-  const int row_len = min(rp1 - rp0, KT);
-  int ktv[4];
+  if (ng > 0 && ng < U) fetch(U0, M0, 0);
+  {
+    const int bd = 64 * KS;
+    for (int i0 = threadIdx.x; i0 < 16 * G; i0 += 4 * bd) {
+      float v[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    ktv[q] = has_res ? a.col_idx[min(rp0 + min((int)threadIdx.x + q * bd, row_len - 1),
-                                     a.n_select - 1)]
-                     : 0;
-
+      for (int q = 0; q < 4; ++q) {
+        const int idx = min(i0 + q * bd, 16 * G - 1);
+        const int mm = idx / G;
+        v[q] = a.sa[(m0 + mm < a.M ? m0 + mm : a.M - 1) * G + (idx - mm * G)];
+      }
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int ia = (int)threadIdx.x + q * bd;
-    if (ia < na) {
-      const int ma = ia / G, j = ia - ma * G;
-      sa_t[j * TM + ma] = (m0 + ma < a.M) ? sav[q] * kInv256 : 0.f;
+      for (int q = 0; q < 4; ++q) {
+        const int idx = i0 + q * bd;
+        if (idx < 16 * G) {
+          const int mm = idx / G, j = idx - mm * G;
+          sa_t[j * 16 + mm] = (m0 + mm < a.M) ? v[q] * kInv256 : 0.f;
+        }
+      }
     }
-    const int iw = (int)threadIdx.x + q * bd;
-    if (iw < nw) {
-      const int r = iw / G, j = iw - r * G;
-      sw_t[j * 16 + r] = swv[q];
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if ((int)threadIdx.x + q * bd < row_len) csr_l[threadIdx.x + q * bd] = ktv[q];
-  // tails of very long K or rows (more than four elements per thread)
-  for (int i = (int)threadIdx.x + 4 * bd; i < row_len; i += bd) csr_l[i] = a.col_idx[rp0 + i];
-  for (int ia = (int)threadIdx.x + 4 * bd; ia < na; ia += bd) {
-    const int ma = ia / G, j = ia - ma * G;
-    sa_t[j * TM + ma] = (m0 + ma < a.M) ? a.sa[(m0 + ma) * G + j] * kInv256 : 0.f;
-  }
-  for (int iw = (int)threadIdx.x + 4 * bd; iw < nw; iw += bd) {
-    const int r = iw / G, j = iw - r * G;
-    sw_t[j * 16 + r] = a.sw[(n0 + r) * G + j];
   }
   __syncthreads();
 
-  // ---- main loop ----
-  // row-relative index of the first entry not yet assigned to a batch:
-  // lower bound of the wave's first block column in the sorted row
-  int e_next = 0;
-  if (has_res) {
+  // ---- the stream (ping-pong buffers, never copied while in flight) ----
+  if (ng > 0) {
+    fetch_sa(U0, M0);
+    for (int t = 0;; t += 2) {
+      bool more = (t + 1) * U < ng + max(nr, 0) || (t + 1) * U < ng;
+      if (!more && (t + 1) * U >= ng) {
+        ensure_nr();
+        more = (t + 1) * U < ng + nr;
+      }
+      fetch(U1, M1, t + 1);
+      fetch_sa(U1, M1);
+      compute(U0, M0);
+      if (!more) break;
+      bool more2 = (t + 2) * U < ng + max(nr, 0) || (t + 2) * U < ng;
+      if (!more2 && (t + 2) * U >= ng) {
+        ensure_nr();
+        more2 = (t + 2) * U < ng + nr;
+      }
+      fetch(U0, M0, t + 2);
+      fetch_sa(U0, M0);
+      compute(U1, M1);
+      if (!more2) break;
+    }
+  }
+
+  // ---- residual entries the window did not show (rows with more than 64
+  // entries up to this wave's last block column; rare): one at a time ----
+  if (ng > 0 && window_full) {
     const int kt0 = gb * kGroup / BLK;
-    for (int c = 0; c < row_len; c += 64) {
-      const int i = c + lane;
-      const int below = __popcll(__ballot(i < row_len && csr_l[i] < kt0));
-      e_next = c + below;
-      if (below < 64) break;
-    }
-  }
-  const int e_first = e_next;
-  bool any_overflow = false;
-  uint4 Xprev[MT][U];
-  int jprev = gb;
-
-  // residual blocks held in slots P, from the batch whose activations are in Xprev
-  auto residual_slots = [&](const Slots& P) {
+    const int kt1 = (gb + ng) * kGroup / BLK;
+    for (int e = wbase + 64; e < rp1; ++e) {
+      const int kt = a.col_idx[e];
+      if (kt >= kt1) break;
+      if (kt < kt0) continue;
+      const int j = kt * BLK / kGroup;
+      const int lo = kt * BLK - j * kGroup;
+      const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK);
+      Unit D;
+      Meta M;
 #pragma unroll
-    for (int s = 0; s < RB; ++s) {
-      if (s < P.n) {
-        const int u = P.j[s] - jprev;
-        if (u >= 0 && u < U && P.j[s] < ge)
-          residual_in(Xprev, u, P.R[s], P.M[s], h2f(P.S[s]), P.e[s], P.j[s]);
+      for (int u = 0; u < U; ++u) {
+        M.j[u] = j;
+        M.e[u] = u == 0 ? e : -2;
+        M.rm[u] = (u == 0 && act) ? 0xFFFFFFFFu : 0u;
+        D.A[u] = ld16(a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + r16) * (BLK / 2) +
+                      (act ? 16 * ch - lo / 2 : 0));
+        D.X[u] = ld16(xrow + (int64_t)j * 64);
+        D.S[u] = a.sr[(int64_t)e * BLK + rrow + r16];
       }
-    }
-  };
-
-  // One pipeline step for batch t held in Dc: prefetch batch t+1 into Dn,
-  // compute batch t, fetch batch t's residual blocks into Sc, then consume
-  // the previous batch's blocks from Sp.  Buffers alternate between steps,
-  // so registers that are still being loaded are never copied.
-  auto step = [&](Dense& Dc, Dense& Dn, Slots& Sc, Slots& Sp, int t) {
-    const int jb = gb + t * U;
-    // Every step issues the same loads (the last prefetch re-reads the final
-    // batch, which is cached), so the compiler's load counters are exact and
-    // computing batch t never waits for batch t+1.
-    fetch_dense(Dn, min(jb + U, gb + (nb - 1) * U));
-    compute_dense(Dc, jb);
-
-    Sc.n = 0;
-    int n_in = 0;
-    if (has_res) {
-      // entries of this batch: [e_next, e_next + n_in) (kt < kt_hi)
-      const int kt_hi = min(jb + U, ge) * kGroup / BLK;
-      for (int c = e_next; c < row_len; c += 64) {
-        const int i = c + lane;
-        const int cnt = __popcll(__ballot(i < row_len && csr_l[i] < kt_hi));
-        n_in += cnt;
-        if (cnt < 64) break;
-      }
-      Sc.n = min(n_in, RB);
-    }
-    // RB slot loads every step (unused slots read a valid cached address)
-#pragma unroll
-    for (int s = 0; s < RB; ++s) {
-      const bool live = s < Sc.n;
-      const int e = rp0 + e_next + s;
-      const int kt = live ? csr_l[e_next + s] : 0;
-      uint32_t rm = 0;
-      const uint8_t* rp = live ? res_ptr(e, kt, rm) : wp;
-      Sc.R[s] = ld16(rp);
-      Sc.M[s] = rm;
-      Sc.S[s] = *(live ? a.sr + (int64_t)e * BLK + rrow + r16 : a.sw);
-      Sc.e[s] = e;
-      Sc.j[s] = kt * BLK / kGroup;
-    }
-    if (has_res) {
-      any_overflow |= n_in > RB;  // blocks past the slots run after the loop
-      e_next += n_in;
-    }
-    residual_slots(Sp);
-#pragma unroll
-    for (int tt = 0; tt < MT; ++tt)
-#pragma unroll
-      for (int u = 0; u < U; ++u) Xprev[tt][u] = Dc.X[tt][u];
-    jprev = jb;
-  };
-
-  Slots S0, S1;
-  S0.n = 0;
-  S1.n = 0;
-  for (int t = 0; t < nb; t += 2) {
-    step(cur, nxt, S0, S1, t);
-    if (t + 1 >= nb) {
-      residual_slots(S0);
-      break;
-    }
-    step(nxt, cur, S1, S0, t + 1);
-    if (t + 2 >= nb) residual_slots(S1);
-  }
-
-  // Cleanup (rare): batches with more than RB residual blocks.  Replays the
-  // batch bookkeeping and runs the blocks past the slots, reloading their
-  // activation fragments (kept out of the pipelined loop so the loop's loads
-  // all have fixed counts).
-  if (any_overflow) {
-    int e = e_first;
-    for (int t = 0; t < nb; ++t) {
-      const int jb = gb + t * U;
-      const int kt_hi = min(jb + U, ge) * kGroup / BLK;
-      int n_in = 0;
-      for (int c = e; c < row_len; c += 64) {
-        const int i = c + lane;
-        const int cnt = __popcll(__ballot(i < row_len && csr_l[i] < kt_hi));
-        n_in += cnt;
-        if (cnt < 64) break;
-      }
-      for (int s = RB; s < n_in; ++s) {
-        const int eg = rp0 + e + s;
-        const int kt = csr_l[e + s];
-        const int js = kt * BLK / kGroup;
-        if (js < jb || js >= jb + U || js >= ge) continue;
-        uint32_t rm;
-        const uint4 R = ld16(res_ptr(eg, kt, rm));
-        uint4 Xg[MT];
-#pragma unroll
-        for (int tt = 0; tt < MT; ++tt) Xg[tt] = ld16(xp[tt] + (int64_t)js * 64);
-        residual(R, rm, h2f(a.sr[(int64_t)eg * BLK + rrow + r16]), eg, js, Xg);
-      }
-      e += n_in;
+      fetch_sa(D, M);
+      compute(D, M);
     }
   }
 
   __syncthreads();  // scales no longer needed: reuse LDS for the reduction
 #pragma unroll
-  for (int t = 0; t < MT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[(wave * TM + t * 16 + 4 * ch + i) * 17 + r16] = y[t][i];
+  for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * ch + i) * 17 + r16] = y[i];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < TM * 16; idx += 64 * KS) {
+  for (int idx = threadIdx.x; idx < 256; idx += 64 * KS) {
     const int mm = idx >> 4, nl = idx & 15;
     float s = 0.f;
 #pragma unroll
-    for (int w = 0; w < KS; ++w) s += red[(w * TM + mm) * 17 + nl];
+    for (int w = 0; w < KS; ++w) s += red[(w * 16 + mm) * 17 + nl];
     const int64_t m = m0 + mm;
     if (m < a.M) a.y[m * a.ldy + n0 + nl] = f2h_bits(s);
   }
 }
 
-template <int BLK, int KS, int MT, int U, bool DUMP>
-hipError_t launch_skinny_cfg(const GemmArgs& a, hipStream_t st) {
-  constexpr int TM = 16 * MT;
+template <int BLK, int KS, int U, bool DUMP>
+hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t st) {
   const int64_t G = a.K / kGroup;
-  const size_t stage = (size_t)G * TM * 4 + (size_t)G * 16 * 2 + (size_t)(a.K / BLK) * 4;
-  const size_t reduce = (size_t)KS * TM * 17 * 4;
+  const size_t stage = (size_t)G * 16 * 4;
+  const size_t reduce = (size_t)KS * 16 * 17 * 4;
   const size_t lds = stage > reduce ? stage : reduce;
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
-  dim3 grid((unsigned)(a.N / 16), (unsigned)((a.M + TM - 1) / TM));
-  hipLaunchKernelGGL((gemm_skinny_kernel<BLK, KS, MT, U, DUMP>), grid, dim3(64 * KS), lds, st, a);
+  dim3 grid((unsigned)(a.N / 16), (unsigned)((a.M + 15) / 16));
+  hipLaunchKernelGGL((gemm_stream_kernel<BLK, KS, U, DUMP>), grid, dim3(64 * KS), lds, st, a);
   return hipGetLastError();
 }
 
+// Waves per tile: enough workgroups to fill the machine, at least one unit
+// of items per wave.
 template <int BLK, bool DUMP>
-hipError_t launch_skinny(const GemmArgs& a, hipStream_t st) {
+hipError_t launch_stream(const GemmArgs& a, hipStream_t st) {
   const int64_t G = a.K / kGroup;
-  if (a.M <= 16) {
-    if (G >= 32) return launch_skinny_cfg<BLK, 8, 1, 4, DUMP>(a, st);
-    return launch_skinny_cfg<BLK, 4, 1, 4, DUMP>(a, st);
-  }
-  if (a.M <= 32) return launch_skinny_cfg<BLK, 4, 2, 2, DUMP>(a, st);
-  return launch_skinny_cfg<BLK, 4, 4, 2, DUMP>(a, st);
+  const int64_t tiles = (a.N / 16) * ((a.M + 15) / 16);
+  if (tiles >= 768 && G >= 8) return launch_stream_cfg<BLK, 4, 4, DUMP>(a, st);
+  if (G >= 32) return launch_stream_cfg<BLK, 8, 4, DUMP>(a, st);
+  if (G >= 8) return launch_stream_cfg<BLK, 4, 4, DUMP>(a, st);
+  return launch_stream_cfg<BLK, 2, 4, DUMP>(a, st);
 }
 
 template <int BLK>
 hipError_t launch_blk(const GemmArgs& a, hipStream_t st) {
-  return a.acc_dump ? launch_skinny<BLK, true>(a, st) : launch_skinny<BLK, false>(a, st);
+  return a.acc_dump ? launch_stream<BLK, true>(a, st) : launch_stream<BLK, false>(a, st);
 }
 
 }  // namespace
