@@ -14,8 +14,10 @@ Printed JSON (one line on stdout):
   value      algorithmic bytes of the step / step time (GB/s), both kernels
   tops       algorithmic integer ops of the step / step time
   roofline   the fused GEMM (dominant kernel): algorithmic bytes (decode) or
-             ops (prefill) per launch / average launch time from HIP events
-             recorded around each launch on the launch stream
+             ops (prefill) per launch / average launch time, from HIP events
+             around K replays of a graph holding only the step's fused GEMMs
+Launches are replayed from HIP graphs (one per rotating set) so the timed
+region measures the GPU, not Python launch overhead (--no-graph: eager).
   cpu_baseline  the CPU oracle (quantise + fused GEMM) on a bounded sample
 """
 from __future__ import annotations
@@ -96,7 +98,13 @@ def traffic_from_profile(wname: str):
 
 
 def cpu_baseline(layers, budget_s: float):
-    """Time the oracle's online path on a bounded sample of the workload."""
+    """Time the oracle's online path (quantise + fused GEMM) on the workload.
+
+    The oracle's packed layers are built first (untimed).  Then whole passes
+    over every (shape, M) of the step are timed until about budget_s seconds
+    of CPU work have accumulated (at least one pass), so the sample is the
+    step itself, repeated; a pass that would exceed four budgets of wall time
+    stops early and the sample names what ran."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -104,30 +112,35 @@ def cpu_baseline(layers, budget_s: float):
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
     from dense_sparse_w4a4_amd import synthetic as syn
-    done, tbytes, tops, tsec = [], 0, 0, 0.0
-    wall0 = time.perf_counter()
+    prepared = []
     for spec, ms in layers:
         w = syn.make_weight(spec)
         xc = syn.make_calib(spec)
         sel, _, _ = oracle.select_blocks(w, xc, spec.block, spec.n_select)
         packed = oracle.pack_weights(w, spec.block, sel)
         for M in ms:
-            x = syn.make_acts(spec, M)
+            prepared.append((spec, M, len(sel), packed, syn.make_acts(spec, M)))
+    tbytes, tops, tsec, passes, partial = 0, 0, 0.0, 0, []
+    while True:
+        for (spec, M, ns, packed, x) in prepared:
             t0 = time.perf_counter()
             qa, sa = oracle.quantize_act(x)
             oracle.fused_gemm(qa, sa, packed)
-            dt = time.perf_counter() - t0
-            tsec += dt
-            tbytes += act_bytes(M, spec.K) + gemm_bytes(M, spec.N, spec.K, spec.block, len(sel))
-            tops += gemm_ops(M, spec.N, spec.K, spec.block, len(sel))
-            done.append(f"{spec.K}x{spec.N}@M={M}")
-            if tsec >= budget_s:
+            tsec += time.perf_counter() - t0
+            tbytes += act_bytes(M, spec.K) + gemm_bytes(M, spec.N, spec.K, spec.block, ns)
+            tops += gemm_ops(M, spec.N, spec.K, spec.block, ns)
+            if passes == 0:
+                partial.append(f"{spec.K}x{spec.N}@M={M}")
+            if tsec > 4 * budget_s:
                 break
-        if tsec >= budget_s or time.perf_counter() - wall0 > 4 * budget_s:
+        passes += 1
+        if tsec >= budget_s or tsec > 4 * budget_s:
             break
+    what = ", ".join(partial)
     return dict(value=tbytes / tsec / 1e9, unit="GB/s", tops=tops / tsec / 1e12, cores=int(threads),
                 kind="oracle", seconds=round(tsec, 3),
-                sample="oracle quantize_act + fused_gemm (numpy, fp64 scales) on " + ", ".join(done))
+                sample=f"{passes} pass(es) of oracle quantize_act + fused_gemm (numpy; BLAS "
+                       f"threads = cores) over {what}")
 
 
 def main():
@@ -136,8 +149,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama3-8b-decode")
-    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--cpu-budget", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
+    ap.add_argument("--per-shape", action="store_true", help="also time each (shape, M) on its own")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter calibration)")
     args = ap.parse_args()
@@ -194,46 +209,80 @@ def main():
     per_step_gemm_bytes = sum(gemm_bytes(M, s.N, s.K, s.block, s.n_select) for s, M in pairs)
     per_step_ops = sum(gemm_ops(M, s.N, s.K, s.block, s.n_select) for s, M in pairs)
 
-    def step(i, events=None):
-        for p, (spec, M, L, x, qa, sa, y) in enumerate(sets[i % R]):
-            ops.quantize_act(x, qa, sa)
-            if events is not None:
-                events[p][0].record()
+    def run_set(i, with_quant=True):
+        for (spec, M, L, x, qa, sa, y) in sets[i % R]:
+            if with_quant:
+                ops.quantize_act(x, qa, sa)
             ops.fused_gemm(qa, sa, L, out=y)
-            if events is not None:
-                events[p][1].record()
 
-    for i in range(args.warmup):
-        step(i)
+    for i in range(max(args.warmup, R)):
+        run_set(i)
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, HIP events around every fused GEMM launch ----
-    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
-            for _ in pairs] for _ in range(args.steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter()
-    start.record()
-    for i in range(args.steps):
-        step(i, evs[i])
-    end.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall
-    total_ms = max(start.elapsed_time(end), wall * 1e3)
-    ms_per_step = total_ms / args.steps
-    gemm_ms = np.array([[e[0].elapsed_time(e[1]) for e in row] for row in evs])  # [steps, pairs]
-    mean_gemm_ms = gemm_ms.mean(axis=0)
+    # One HIP graph per rotating set: the whole step (act-quant + fused GEMM
+    # for every (shape, M)), and the fused GEMMs alone for per-launch timing.
+    use_graph = not args.no_graph
+    if use_graph:
+        g_step, g_gemm = [], []
+        cap = torch.cuda.Stream()
+        for r in range(R):
+            for lst, wq in ((g_step, True), (g_gemm, False)):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    run_set(r, wq)
+                lst.append(g)
+        torch.cuda.synchronize()
+        for r in range(R):
+            g_step[r].replay()
+        torch.cuda.synchronize()
 
-    for p, (spec, M) in enumerate(pairs):
-        gb = gemm_bytes(M, spec.N, spec.K, spec.block, spec.n_select)
-        go = gemm_ops(M, spec.N, spec.K, spec.block, spec.n_select)
-        t = mean_gemm_ms[p] * 1e-3
-        log(f"[bench]   K={spec.K:6d} N={spec.N:6d} M={M:5d}: gemm {t * 1e6:8.2f} us  "
-            f"{gb / t / 1e9:8.1f} GB/s ({gb / t / 1e9 / HBM_PEAK_GBS:5.1%} HBM)  "
-            f"{go / t / 1e12:8.2f} TOPS ({go / t / 1e12 / INT8_MFMA_PEAK_TOPS:5.1%} int8 MFMA)")
+    def timed(n, body):
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter()
+        start.record()
+        for i in range(n):
+            body(i)
+        end.record()
+        torch.cuda.synchronize()
+        return max(start.elapsed_time(end), 0.0), (time.perf_counter() - wall) * 1e3
+
+    # ---- timed region: exactly K steps ----
+    if use_graph:
+        ev_ms, wall_ms = timed(args.steps, lambda i: g_step[i % R].replay())
+    else:
+        ev_ms, wall_ms = timed(args.steps, lambda i: run_set(i))
+    ms_per_step = ev_ms / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step on HIP events "
+        f"({wall_ms / args.steps * 1e3:.2f} us/step wall), graphs={'on' if use_graph else 'off'}")
+
+    # ---- fused GEMM alone: average launch time over the same number of steps ----
+    if use_graph:
+        gem_ms, _ = timed(args.steps, lambda i: g_gemm[i % R].replay())
+    else:
+        gem_ms, _ = timed(args.steps, lambda i: run_set(i, False))
+    gemm_time_s = gem_ms * 1e-3 / args.steps  # per step (all pairs)
+
+    # per-(shape, M) launch times, each pair replayed in its own graph
+    if args.per_shape and use_graph:
+        for p_idx, (spec, M) in enumerate(pairs):
+            gs = []
+            for r in range(R):
+                (sp_, M_, L, x, qa, sa, y) = sets[r][p_idx]
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    for _ in range(8):
+                        ops.fused_gemm(qa, sa, L, out=y)
+                gs.append(g)
+            t_ms, _ = timed(20, lambda i: gs[i % R].replay())
+            t = t_ms * 1e-3 / (20 * 8)
+            gb = gemm_bytes(M, spec.N, spec.K, spec.block, spec.n_select)
+            go = gemm_ops(M, spec.N, spec.K, spec.block, spec.n_select)
+            log(f"[bench]   K={spec.K:6d} N={spec.N:6d} M={M:5d}: gemm {t * 1e6:8.2f} us  "
+                f"{gb / t / 1e9:8.1f} GB/s ({gb / t / 1e9 / HBM_PEAK_GBS:5.1%} HBM)  "
+                f"{go / t / 1e12:8.2f} TOPS ({go / t / 1e12 / INT8_MFMA_PEAK_TOPS:5.1%} int8 MFMA)")
 
     launches = len(pairs)
-    gemm_time_s = float(mean_gemm_ms.sum()) * 1e-3
     if bound == "hbm":
         achieved = per_step_gemm_bytes / gemm_time_s / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
@@ -243,7 +292,7 @@ def main():
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_MFMA_PEAK_TOPS,
                     unit="TOP/s", frac=round(achieved / INT8_MFMA_PEAK_TOPS, 4))
     roof["traffic"] = traffic_from_profile(args.workload)
-    roof["kernel"] = "gemm_skinny_kernel"
+    roof["kernel"] = "gemm_stream_kernel"
     roof["avg_launch_us"] = round(gemm_time_s / launches * 1e6, 3)
     roof["alg_bytes_per_launch"] = per_step_gemm_bytes / launches
     roof["alg_ops_per_launch"] = per_step_ops / launches
@@ -277,6 +326,7 @@ def main():
             "codes": "w4a4 int4 symmetric, int8 MFMA, int32 accumulators, fp32 epilogue, fp16 out",
             "bytes_per_step": per_step_bytes, "ops_per_step": per_step_ops,
             "rotating_copies": R,
+            "launch": "hip-graph" if use_graph else "eager",
         },
         "roofline": roof,
     }
