@@ -23,29 +23,11 @@
 // always inside one group at a 32-aligned offset) covers whole chunks, so its
 // MFMAs reuse the activation registers already loaded for the dense base in
 // the same group (the "zipper"); chunks outside the block feed zeros.
-#include "mq_internal.h"
+#include "gemm_common.h"
 
 namespace mq {
 namespace {
 
-__device__ __forceinline__ v4i widen8(uint32_t lo, uint32_t hi) {
-  v4i r;
-  r[0] = (int)((lo << 4) & 0xF0F0F0F0u);
-  r[1] = (int)(lo & 0xF0F0F0F0u);
-  r[2] = (int)((hi << 4) & 0xF0F0F0F0u);
-  r[3] = (int)(hi & 0xF0F0F0F0u);
-  return r;
-}
-
-__device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
-
-constexpr float kInv256 = 1.0f / 256.0f;
 
 // Streaming tile for small M: 16 output channels x 16 tokens per workgroup
 // (grid.y walks 16-token tiles).  The KS waves of a workgroup split the K
@@ -353,6 +335,9 @@ hipError_t launch_blk(const GemmArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st) {
+  // large M: LDS-tiled MFMA kernel (weights read once per 128-token tile);
+  // small M: the streaming kernel (weights read once per 16-token tile)
+  if (a.M > 32) return launch_tile_gemm(a, st);
   switch (a.block) {
     case 32: return launch_blk<32>(a, st);
     case 64: return launch_blk<64>(a, st);

@@ -94,5 +94,6 @@ struct GemmArgs {
 };
 
 hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st);
+hipError_t launch_tile_gemm(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mq

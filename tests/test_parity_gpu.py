@@ -120,6 +120,12 @@ GEMM_CASES = [
     (16, 512, 512, 64, 0.0),
     (70, 256, 1024, 64, 0.10),
     (2, 64, 2048, 32, 0.05),
+    # large-M tile kernel: 32-wide blocks, partial channel tiles, ragged M
+    (100, 256, 512, 32, 0.30),
+    (130, 96, 384, 32, 0.20),
+    (257, 192, 256, 64, 0.15),
+    (64, 128, 1024, 128, 0.25),
+    (33, 64, 128, 64, 1.00),
 ]
 
 
