@@ -9,6 +9,9 @@ objects are linked into dense_sparse_w4a4_amd/libmosaicq.so.  Flags:
   -fhip-fp32-correctly-rounded-divide-sqrt   IEEE fp32 division (the default,
                         stated explicitly because codes depend on it)
   -packed-fp32-ops off  no packed fp32 VALU instructions are generated
+  -amdgpu-mfma-vgpr-form  MFMA operands and results live in ordinary VGPRs
+                        (kernels sized for one wave per SIMD would otherwise
+                        route every accumulator through AGPR copies)
 """
 from __future__ import annotations
 
@@ -30,6 +33,7 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
@@ -57,7 +61,7 @@ def build(verbose: bool = True) -> str:
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(_compile, srcs))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Wl,--no-undefined", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)

@@ -336,8 +336,9 @@ hipError_t launch_blk(const GemmArgs& a, hipStream_t st) {
 
 hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st) {
   // large M: LDS-tiled MFMA kernel (weights read once per 128-token tile);
-  // small M: the streaming kernel (weights read once per 16-token tile)
-  if (a.M > 32) return launch_tile_gemm(a, st);
+  // small M, or a K too long for the tile kernel's LDS table: the streaming
+  // kernel (weights read once per 16-token tile)
+  if (a.M > 32 && tile_gemm_fits(a)) return launch_tile_gemm(a, st);
   switch (a.block) {
     case 32: return launch_blk<32>(a, st);
     case 64: return launch_blk<64>(a, st);

@@ -6,21 +6,33 @@
 //
 // Tile: 128 tokens x 128 output channels per workgroup of four waves (2 x 2,
 // 64 x 64 each, sixteen 16x16 MFMA tiles per wave).  One K step is one
-// 128-channel group.  Per group the workgroup stages, in a register buffer
-// and then in LDS:
+// 128-channel group.  Per group the workgroup stages, through a register
+// buffer into LDS:
 //   A  activation codes, 128 rows x 64 bytes
 //   B  weight codes,     128 rows x 64 bytes
 //   R  residual codes for the same 128 channels (zero where no block is
 //      selected), 128 rows x 64 bytes
-//   the activation scales (x 1/256), weight scales and residual row scales.
-// LDS holds each 16x16 fragment in MFMA lane order (slot = tile*64 + lane,
-// 16 bytes), so every fragment read is one conflict-free 16-byte LDS read.
+//   the activation scales, weight scales and residual row scales.
+// Codes are widened to int8 once, while being written to LDS, and LDS holds
+// each MFMA operand in lane order (slot = (tile*2 + half)*64 + lane, 16
+// bytes), so every operand read is one conflict-free 16-byte LDS read.  In
+// staging, lane l of a wave handles row l%16 of a 16-row slab and 16-byte
+// piece l/16, so the 16 lanes of a piece write 256 consecutive bytes.
 //
 // K layout inside a group: lane chunk c = lane/16 feeds the first MFMA with
 // channels [16c, 16c+16) and the second with [64+16c, 64+16c+16).  A 64-wide
 // residual block therefore lines up with exactly one of the two MFMAs, a
 // 32-wide block with one MFMA on half of the lanes, a 128-wide block with
 // both, and each block keeps its own accumulator and row scale.
+//
+// Epilogue: per 16x16 tile and group, y += (sa[m]*sw[n]) * acc[m][n].  The
+// 256 scale products of a tile form an outer product, so the matrix core
+// computes them with one bf16 MFMA: sa (fp32) is split exactly into three
+// bf16 parts and sw (fp16) into two, the six partial products go to six k
+// slots, and the fp32 accumulation returns sa*sw to within a few fp32 ulps
+// over the whole fp32 range.  The vector unit keeps one int->float
+// conversion and one FMA per element and group.  The factor 256 carried by
+// the widened codes is removed once, at the final store.
 //
 // Pipeline: group g passes through register buffer g%2 and LDS stage g%2.
 // While the waves compute group j from LDS, the loads of groups j+1 and j+2
@@ -32,38 +44,97 @@
 namespace mq {
 namespace {
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
 constexpr int TBM = 128;  // tokens per tile
 constexpr int TBN = 128;  // output channels per tile
+constexpr size_t kMaxLds = 80 * 1024;  // two workgroups per CU
 
 template <int BLK>
 struct TileCfg {
-  static constexpr int NBR = TBN / BLK;                    // block rows in a tile
-  static constexpr int NBC = kGroup / BLK;                 // block columns in a group
-  static constexpr int NSR = (TBN * NBC + 255) / 256;      // scale loads per thread
-  static constexpr int SRS = NSR * 256;                    // residual-scale slots per stage
+  static constexpr int NBR = TBN / BLK;                // block rows in a tile
+  static constexpr int NBC = kGroup / BLK;             // block columns in a group
+  static constexpr int NSR = (TBN * NBC + 255) / 256;  // residual-scale loads per thread
+  static constexpr int SRS = NSR * 256;                // residual-scale slots per stage
+  static constexpr int OPB = 8 * 2 * 64 * 16;          // bytes of one widened operand tile
+  static constexpr int STAGE = 3 * OPB + (TBM + TBN + SRS) * 16;
+  static size_t lds(int64_t K) { return (size_t)STAGE + (size_t)NBR * (size_t)(K / BLK) * 2; }
 };
 
+// Register buffer of one group.  Residual pieces and scales of blocks that
+// are not selected are loaded from a dummy address; compute reads the
+// residual operand and scale of a block column only when the block is
+// selected, so that data is never used and needs no mask.
+template <int NSR>
 struct Stage {
   uint4 A[2], B[2], R[2];
-  uint32_t rm[2];        // residual piece present (all-ones) or absent (zero)
-  uint32_t sc;           // activation scale bits (waves 0-1) or weight scale (2-3)
-  uint32_t sr[2];        // residual row scale bits (raw load)
-  uint32_t srm[2];       // all-ones where that residual scale exists
+  uint32_t sc;       // activation scale bits (waves 0-1) or weight scale bits (waves 2-3)
+  uint32_t sr[NSR];  // residual row scale bits
 };
 
+// LDS access through 32-bit LDS addresses, so that constant offsets fold
+// into the instructions' offset fields.
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+typedef __attribute__((address_space(3))) v2u lds_v2u;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ v4i lds_ld16(uint32_t a) { return *(const lds_v4i*)(uintptr_t)a; }
+__device__ __forceinline__ uint2 lds_ld8(uint32_t a) {
+  const v2u v = *(const lds_v2u*)(uintptr_t)a;
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void lds_st16(uint32_t a, v4i v) { *(lds_v4i*)(uintptr_t)a = v; }
+__device__ __forceinline__ void lds_st16u(uint32_t a, uint4 v) {
+  const v4i w = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+  *(lds_v4i*)(uintptr_t)a = w;
+}
+
+__device__ __forceinline__ v4f mfma_scale(v4s a, v4s b) {
+  const v4f z = {0.f, 0.f, 0.f, 0.f};
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, z, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t bf16_trunc(float f) { return __float_as_uint(f) & 0xFFFF0000u; }
+
+// Scale-product operands, one 16-byte slot per token row / channel.  A lane
+// in chunk 0 reads the first 8 bytes (k slots 0-3), chunk 1 the last 8
+// (k slots 4-7); chunks 2-3 supply zeros.
+//   token:   {a1,a1, a2,a2 | a3,a3, 0,0}   with sa = a1 + a2 + a3 exactly
+//   channel: {w1,w2, w1,w2 | w1,w2, 0,0}   with s  = w1 + w2 exactly
+// Truncating to 8 significant bits leaves a remainder of at most 16 bits,
+// and its truncation one of at most 8, so the parts are exact.
+__device__ __forceinline__ uint4 token_scale_slot(float s) {
+  const uint32_t a1 = bf16_trunc(s);
+  const float r1 = s - __uint_as_float(a1);
+  const uint32_t a2 = bf16_trunc(r1);
+  const uint32_t a3 = bf16_trunc(r1 - __uint_as_float(a2));
+  return make_uint4((a1 >> 16) | a1, (a2 >> 16) | a2, (a3 >> 16) | a3, 0u);
+}
+
+__device__ __forceinline__ uint4 channel_scale_slot(uint16_t hbits) {
+  const float s = h2f(hbits);
+  const uint32_t w1 = bf16_trunc(s);
+  const uint32_t w2 = bf16_trunc(s - __uint_as_float(w1));
+  const uint32_t v = (w1 >> 16) | w2;
+  return make_uint4(v, v, v, 0u);
+}
+
 template <int BLK, bool DUMP>
-__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(GemmArgs a) {
+__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   using C = TileCfg<BLK>;
   extern __shared__ __align__(16) unsigned char smem[];
-  constexpr int SA = 64 * 8 * 16;  // bytes of one staged operand tile (8 tiles x 64 lanes x 16 B)
-  constexpr int STAGE = 3 * SA + TBM * 4 + TBN * 2 + C::SRS * 2;
   const int G = (int)(a.K / kGroup);
   const int KT = (int)(a.K / BLK);
-  uint16_t* tab = reinterpret_cast<uint16_t*>(smem + 2 * STAGE);  // [NBR][KT]: entry-rp+1, 0 = none
+  uint16_t* tab = reinterpret_cast<uint16_t*>(smem + C::STAGE);  // [NBR][KT]: entry-rp+1, 0 = none
   __shared__ int rp_row[C::NBR];
 
   const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // (& 3 makes the range known, so LDS offsets fold into the instructions)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
   const int lane = tid & 63;
   const int r16 = lane & 15;
   const int ch = lane >> 4;
@@ -104,80 +175,91 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(GemmArgs a) {
   __syncthreads();
 
   // ---- staging: global -> registers (fixed load count) ----
-  auto load = [&](Stage& S, int j) {
+  // Per-thread offsets are fixed for the whole K loop; each group adds a
+  // uniform step to a uniform base (32-bit offsets: the host routes
+  // operands of 4 GiB or more to the streaming kernel).  Pieces and scales
+  // of blocks that are not selected read offset 0 of a valid buffer.
+  const uint8_t* rbase = a.n_select > 0 ? a.qr : a.qw;
+  const uint8_t* sbase = a.n_select > 0 ? reinterpret_cast<const uint8_t*>(a.sr)
+                                        : reinterpret_cast<const uint8_t*>(a.sw);
+  uint32_t offA[2], offB[2];
+  int tabR[2], baseR[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * (wave + 4 * i) + r16, p = ch;  // row, 16-byte piece
+    const int64_t m = min(m0 + r, a.M - 1);
+    const int64_t n = min(n0 + r, a.N - 1);
+    offA[i] = (uint32_t)(m * Kh + p * 16);
+    offB[i] = (uint32_t)(n * Kh + p * 16);
+    const int rb = (int)(n / BLK) - nt0;
+    tabR[i] = rb * KT + (p * 32) / BLK;
+    baseR[i] = (rp_row[rb] - 1) * (BLK * BLK / 2) + (int)(n - (int64_t)(nt0 + rb) * BLK) * (BLK / 2) +
+               ((p * 32) % BLK) / 2;
+  }
+  int tabS[C::NSR], baseS[C::NSR];
+#pragma unroll
+  for (int i = 0; i < C::NSR; ++i) {
+    const int idx = tid + 256 * i;
+    const int r = idx / C::NBC, c = idx % C::NBC;
+    const int64_t n = min(n0 + min(r, TBN - 1), a.N - 1);
+    const int rb = (int)(n / BLK) - nt0;
+    tabS[i] = idx < TBN * C::NBC ? rb * KT + c : -1;
+    baseS[i] = ((rp_row[rb] - 1) * BLK + (int)(n - (int64_t)(nt0 + rb) * BLK)) * 2;
+  }
+  const uint32_t offS = wave < 2 ? (uint32_t)(min(m0 + tid, a.M - 1) * G * 4)
+                                 : (uint32_t)(min(n0 + (tid - 128), a.N - 1) * G * 2);
+
+  auto load = [&](Stage<C::NSR>& S, int j) {
     j = min(j, G - 1);
+    const uint8_t* qa_j = a.qa + j * 64;
+    const uint8_t* qw_j = a.qw + j * 64;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int q = tid + 256 * i;
-      const int r = q >> 2, p = q & 3;
-      const int64_t m = min(m0 + r, a.M - 1);
-      const int64_t n = min(n0 + r, a.N - 1);
-      S.A[i] = ld16(a.qa + m * Kh + j * 64 + p * 16);
-      S.B[i] = ld16(a.qw + n * Kh + j * 64 + p * 16);
-      const int rb = (int)(n / BLK) - nt0;
-      const int kg = j * kGroup + p * 32;
-      const int kt = kg / BLK;
-      const int ent = (a.n_select > 0) ? (int)tab[rb * KT + kt] : 0;
-      const uint8_t* rp = a.qw;
-      if (ent > 0) {
-        const int64_t e = rp_row[rb] + ent - 1;
-        rp = a.qr + e * (BLK * BLK / 2) + (n - (int64_t)(nt0 + rb) * BLK) * (BLK / 2) + (kg - kt * BLK) / 2;
-      }
-      S.R[i] = ld16(rp);
-      S.rm[i] = ent > 0 ? 0xFFFFFFFFu : 0u;
+      S.A[i] = ld16(qa_j + offA[i]);
+      S.B[i] = ld16(qw_j + offB[i]);
+      const int ent = a.n_select > 0 ? (int)tab[tabR[i] + j * C::NBC] : 0;
+      S.R[i] = ld16(rbase + (uint32_t)(ent > 0 ? ent * (BLK * BLK / 2) + baseR[i] : 0));
     }
     if (wave < 2) {
-      S.sc = __float_as_uint(a.sa[min(m0 + tid, a.M - 1) * G + j]);
+      S.sc = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.sa) + j * 4 + offS);
     } else {
-      S.sc = a.sw[min(n0 + (tid - 128), a.N - 1) * G + j];
+      S.sc = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.sw) + j * 2 + offS);
     }
 #pragma unroll
     for (int i = 0; i < C::NSR; ++i) {
-      const int idx = tid + 256 * i;
-      const int r = idx / C::NBC, c = idx % C::NBC;
-      const int64_t n = min(n0 + min(r, TBN - 1), a.N - 1);
-      const int rb = (int)(n / BLK) - nt0;
-      const int ent = (a.n_select > 0 && idx < TBN * C::NBC) ? (int)tab[rb * KT + j * C::NBC + c] : 0;
-      const uint16_t* sp = a.sw;
-      if (ent > 0) sp = a.sr + (int64_t)(rp_row[rb] + ent - 1) * BLK + (n - (int64_t)(nt0 + rb) * BLK);
-      S.sr[i] = (uint32_t)(*sp);  // combined with the mask at the LDS store, not here,
-      S.srm[i] = ent > 0 ? 0xFFFFFFFFu : 0u;  // so the load is not waited on early
+      const int ent = (a.n_select > 0 && tabS[i] >= 0) ? (int)tab[tabS[i] + j * C::NBC] : 0;
+      S.sr[i] = *reinterpret_cast<const uint16_t*>(sbase + (uint32_t)(ent > 0 ? ent * (BLK * 2) + baseS[i] : 0));
     }
   };
 
-  // registers -> LDS stage (fragment lane order)
-  auto store = [&](unsigned char* st, const Stage& S) {
-    unsigned char* As = st;
-    unsigned char* Bs = st + SA;
-    unsigned char* Rs = st + 2 * SA;
-    float* sas = reinterpret_cast<float*>(st + 3 * SA);
-    uint16_t* sws = reinterpret_cast<uint16_t*>(st + 3 * SA + TBM * 4);
-    uint16_t* srs = reinterpret_cast<uint16_t*>(st + 3 * SA + TBM * 4 + TBN * 2);
+  // registers -> LDS stage: widened operands in lane order, scale operands
+  uint32_t slotW[2];  // byte offset of this thread's first widened slot, per row slab
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * (wave + 4 * i) + r16, p = ch;  // row, 16-byte piece
+    const int h = p >> 1, c0 = (p & 1) * 2;
+    slotW[i] = (uint32_t)((((r >> 4) * 2 + h) * 64 + (r & 15) + 16 * c0) * 16);
+  }
+  auto store = [&](uint32_t st, const Stage<C::NSR>& S) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int q = tid + 256 * i;
-      const int r = q >> 2, p = q & 3;
-      const int h = p >> 1, c0 = (p & 1) * 2;
-      const int slot = (r >> 4) * 64 + (r & 15) + 16 * c0;
-      const int o0 = slot * 16 + h * 8, o1 = (slot + 16) * 16 + h * 8;
-      *reinterpret_cast<uint2*>(As + o0) = make_uint2(S.A[i].x, S.A[i].y);
-      *reinterpret_cast<uint2*>(As + o1) = make_uint2(S.A[i].z, S.A[i].w);
-      *reinterpret_cast<uint2*>(Bs + o0) = make_uint2(S.B[i].x, S.B[i].y);
-      *reinterpret_cast<uint2*>(Bs + o1) = make_uint2(S.B[i].z, S.B[i].w);
-      const uint32_t rm = S.rm[i];
-      *reinterpret_cast<uint2*>(Rs + o0) = make_uint2(S.R[i].x & rm, S.R[i].y & rm);
-      *reinterpret_cast<uint2*>(Rs + o1) = make_uint2(S.R[i].z & rm, S.R[i].w & rm);
+      const uint32_t b = st + slotW[i];
+      lds_st16(b, widen8(S.A[i].x, S.A[i].y));
+      lds_st16(b + 256, widen8(S.A[i].z, S.A[i].w));
+      lds_st16(b + C::OPB, widen8(S.B[i].x, S.B[i].y));
+      lds_st16(b + C::OPB + 256, widen8(S.B[i].z, S.B[i].w));
+      lds_st16(b + 2 * C::OPB, widen8(S.R[i].x, S.R[i].y));
+      lds_st16(b + 2 * C::OPB + 256, widen8(S.R[i].z, S.R[i].w));
     }
+    const uint32_t sl = st + 3 * C::OPB + (uint32_t)tid * 16;
     if (wave < 2) {
-      sas[tid] = (m0 + tid < a.M) ? __uint_as_float(S.sc) * kInv256 : 0.f;
+      lds_st16u(sl, token_scale_slot((m0 + tid < a.M) ? __uint_as_float(S.sc) : 0.f));
     } else {
-      sws[tid - 128] = (uint16_t)S.sc;
+      lds_st16u(sl, channel_scale_slot((uint16_t)S.sc));  // channel slots follow the token slots
     }
 #pragma unroll
-    for (int i = 0; i < C::NSR; ++i) {
-      const int idx = tid + 256 * i;
-      srs[idx] = (uint16_t)(S.sr[i] & S.srm[i]);  // slots past TBN*NBC are padding
-    }
+    for (int i = 0; i < C::NSR; ++i)  // slots past TBN*NBC are padding
+      lds_st16u(sl + (TBM + TBN) * 16 + i * 4096, channel_scale_slot((uint16_t)S.sr[i]));
   };
 
   const int wm = wave >> 1, wn = wave & 1;
@@ -189,123 +271,160 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[i][q][e] = 0.f;
   const v4i zero = {0, 0, 0, 0};
+  // The scale MFMA sums k slots 0-15; slots 8-15 (lanes 32-63) must add
+  // nothing.  Only the channel side is zeroed there: the token side holds
+  // finite values, and finite x 0 = 0.
+  const uint32_t chan_mask = ch < 2 ? 0xFFFFFFFFu : 0u;
+  const uint32_t scale_off = (uint32_t)(ch & 1) * 8;
 
-  auto compute = [&](const unsigned char* st, int j) {
-    const unsigned char* As = st;
-    const unsigned char* Bs = st + SA;
-    const unsigned char* Rs = st + 2 * SA;
-    const float* sas = reinterpret_cast<const float*>(st + 3 * SA);
-    const uint16_t* sws = reinterpret_cast<const uint16_t*>(st + 3 * SA + TBM * 4);
-    const uint16_t* srs = reinterpret_cast<const uint16_t*>(st + 3 * SA + TBM * 4 + TBN * 2);
-    v4i Alo[4], Ahi[4];
-    float4 sa4[4];
+  auto epi = [](float (&yt)[4], const v4f& P, const v4i& acc) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) yt[e] = fmaf(P[e], (float)acc[e], yt[e]);
+  };
+
+  // residual-table lookups of this wave for group j: lane q*NBC + c holds
+  // the entry of column tile q, block column c (0 = not selected)
+  const int tq = min(lane / C::NBC, 3), tc = lane % C::NBC;
+  const int tnt = (int)((n0 + (wn * 4 + tq) * 16) / BLK);
+  const bool tvalid = lane < 4 * C::NBC && tnt < nrows_b;
+  const int tidx = tvalid ? (tnt - nt0) * KT + tc : 0;
+
+  auto compute = [&](uint32_t st, int j) {
+    // Lane offsets are recomputed from an opaque copy in every step, so the
+    // per-tile constants fold into the LDS instructions' offset fields
+    // instead of being hoisted out of the loop as one register per tile.
+    // Bases include the wave's tile row / column, so only compile-time
+    // constants remain in the per-tile addresses.
+    uint32_t la = st + (uint32_t)lane * 16u + (uint32_t)wm * 8192u;
+    uint32_t lb = st + C::OPB + (uint32_t)lane * 16u + (uint32_t)wn * 8192u;
+    uint32_t sa_b = st + 3 * C::OPB + (uint32_t)r16 * 16u + scale_off + (uint32_t)wm * 1024u;
+    uint32_t sw_b = st + 3 * C::OPB + TBM * 16 + (uint32_t)r16 * 16u + scale_off + (uint32_t)wn * 1024u;
+    asm volatile("" : "+v"(la), "+v"(lb), "+v"(sa_b), "+v"(sw_b));
+    int ent_l = 0;
+    if (a.n_select > 0) ent_l = tvalid ? (int)tab[tidx + j * C::NBC] : 0;
+    v4i A0[4], A1[4];
+    v4s sa_op[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int tm = wm * 4 + i;
-      const uint4 v = *reinterpret_cast<const uint4*>(As + (tm * 64 + lane) * 16);
-      Alo[i] = widen8(v.x, v.y);
-      Ahi[i] = widen8(v.z, v.w);
-      sa4[i] = *reinterpret_cast<const float4*>(sas + tm * 16 + 4 * ch);
+      A0[i] = lds_ld16(la + (i * 2 + 0) * 1024);
+      A1[i] = lds_ld16(la + (i * 2 + 1) * 1024);
+      sa_op[i] = __builtin_bit_cast(v4s, lds_ld8(sa_b + i * 256));
     }
+    const uint64_t pres = __builtin_amdgcn_ballot_w64(ent_l > 0);
+    auto chan_op = [&](uint32_t addr) {
+      const uint2 v = lds_ld8(addr);
+      return __builtin_bit_cast(v4s, make_uint2(v.x & chan_mask, v.y & chan_mask));
+    };
+    v4i Bn0 = lds_ld16(lb);
+    v4i Bn1 = lds_ld16(lb + 1024);
+    uint2 swn = lds_ld8(sw_b);
+    // Per 16-channel column q: the dense tiles run as a two-deep software
+    // pipeline (the MFMAs of tile i are issued before the epilogue of tile
+    // i-1), with scheduling barriers so that at most two tiles' products are
+    // live and the accumulators stay in VGPRs.
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int tn = wn * 4 + q;
-      const uint4 v = *reinterpret_cast<const uint4*>(Bs + (tn * 64 + lane) * 16);
-      const v4i Blo = widen8(v.x, v.y), Bhi = widen8(v.z, v.w);
-      const float sw = h2f(sws[tn * 16 + r16]);
-      v4i acc[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc[i] = mfma(Alo[i], Blo, zero);
-        acc[i] = mfma(Ahi[i], Bhi, acc[i]);
+      const v4i B0 = Bn0, B1 = Bn1;
+      const v4s sw_op = __builtin_bit_cast(v4s, make_uint2(swn.x & chan_mask, swn.y & chan_mask));
+      if (q < 3) {  // next column's operands
+        Bn0 = lds_ld16(lb + ((q + 1) * 2 + 0) * 1024);
+        Bn1 = lds_ld16(lb + ((q + 1) * 2 + 1) * 1024);
+        swn = lds_ld8(sw_b + (q + 1) * 256);
       }
+      v4i acc[4];
+      v4f P[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        y[i][q][0] = fmaf(sa4[i].x * sw, (float)acc[i][0], y[i][q][0]);
-        y[i][q][1] = fmaf(sa4[i].y * sw, (float)acc[i][1], y[i][q][1]);
-        y[i][q][2] = fmaf(sa4[i].z * sw, (float)acc[i][2], y[i][q][2]);
-        y[i][q][3] = fmaf(sa4[i].w * sw, (float)acc[i][3], y[i][q][3]);
-        if (DUMP) {
-          const int64_t n = n0 + tn * 16 + r16;
+        acc[i] = mfma(A0[i], B0, zero);
+        acc[i] = mfma(A1[i], B1, acc[i]);
+        P[i] = mfma_scale(sa_op[i], sw_op);
+        if (i > 0) epi(y[i - 1][q], P[i - 1], acc[i - 1]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      epi(y[3][q], P[3], acc[3]);
+      if (DUMP) {
+        const int64_t n = n0 + tn * 16 + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int64_t m = m0 + (wm * 4 + i) * 16 + 4 * ch + e;
             if (m < a.M && n < a.N) a.acc_dump[(m * a.N + n) * G + j] = acc[i][e] >> 8;
           }
-        }
       }
-      // zipper: residual blocks of these 16 channels in group j
-      const int nt = (int)((n0 + tn * 16) / BLK);
-      const int rb = nt - nt0;
-      if (a.n_select > 0 && nt < nrows_b) {
-        const uint4 rv = *reinterpret_cast<const uint4*>(Rs + (tn * 64 + lane) * 16);
+      // zipper: residual blocks of these 16 channels in group j, against
+      // the same activation operands
+      if ((pres >> (q * C::NBC)) & ((1u << C::NBC) - 1u)) {
+        const int nt = (int)((n0 + tn * 16) / BLK);
+        const int rb = nt - nt0;
 #pragma unroll
         for (int c = 0; c < C::NBC; ++c) {
-          const int ent = __builtin_amdgcn_readfirstlane((int)tab[rb * KT + j * C::NBC + c]);
-          if (ent == 0) continue;
-          const float srf = h2f(srs[(tn * 16 + r16) * C::NBC + c]);
-          v4i racc[4];
-          if (BLK == 128) {
-            const v4i Rlo = widen8(rv.x, rv.y), Rhi = widen8(rv.z, rv.w);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              racc[i] = mfma(Alo[i], Rlo, zero);
-              racc[i] = mfma(Ahi[i], Rhi, racc[i]);
-            }
-          } else if (BLK == 64) {
-            const v4i R = (c == 0) ? widen8(rv.x, rv.y) : widen8(rv.z, rv.w);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) racc[i] = mfma(c == 0 ? Alo[i] : Ahi[i], R, zero);
-          } else {
-            // 32-wide block c: MFMA half c/2, lane chunks 2*(c%2), 2*(c%2)+1
-            const uint32_t msk = ((ch >> 1) == (c & 1)) ? 0xFFFFFFFFu : 0u;
-            const v4i R = (c < 2) ? widen8(rv.x & msk, rv.y & msk) : widen8(rv.z & msk, rv.w & msk);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) racc[i] = mfma(c < 2 ? Alo[i] : Ahi[i], R, zero);
-          }
+          if (!((pres >> (q * C::NBC + c)) & 1u)) continue;
+          // (rare path: the residual bases are formed here)
+          const v4s sr_op = chan_op(st + 3 * C::OPB + (TBM + TBN) * 16 +
+                                    (uint32_t)((tn * 16 + r16) * C::NBC + c) * 16 + scale_off);
+          const v4i R0 = lds_ld16(lb + C::OPB + (q * 2 + 0) * 1024);
+          const v4i R1 = lds_ld16(lb + C::OPB + (q * 2 + 1) * 1024);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            y[i][q][0] = fmaf(sa4[i].x * srf, (float)racc[i][0], y[i][q][0]);
-            y[i][q][1] = fmaf(sa4[i].y * srf, (float)racc[i][1], y[i][q][1]);
-            y[i][q][2] = fmaf(sa4[i].z * srf, (float)racc[i][2], y[i][q][2]);
-            y[i][q][3] = fmaf(sa4[i].w * srf, (float)racc[i][3], y[i][q][3]);
-            if (DUMP) {
-              const int64_t e_g = rp_row[rb] + ent - 1;
-              const int rr = (int)(n0 + tn * 16 + r16 - (int64_t)nt * BLK);
+            if (BLK == 128) {
+              acc[i] = mfma(A0[i], R0, zero);
+              acc[i] = mfma(A1[i], R1, acc[i]);
+            } else if (BLK == 64) {
+              acc[i] = (c == 0) ? mfma(A0[i], R0, zero) : mfma(A1[i], R1, zero);
+            } else {
+              // 32-wide block c: MFMA half c/2, lane chunks 2*(c%2), 2*(c%2)+1
+              const int msk = ((ch >> 1) == (c & 1)) ? -1 : 0;
+              const v4i Rm = ((c < 2) ? R0 : R1) & msk;
+              acc[i] = mfma((c < 2) ? A0[i] : A1[i], Rm, zero);
+            }
+            P[i] = mfma_scale(sa_op[i], sr_op);
+            if (i > 0) epi(y[i - 1][q], P[i - 1], acc[i - 1]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          epi(y[3][q], P[3], acc[3]);
+          if (DUMP) {
+            const int ent = __builtin_amdgcn_readlane(ent_l, q * C::NBC + c);
+            const int64_t e_g = rp_row[rb] + ent - 1;
+            const int rr = (int)(n0 + tn * 16 + r16 - (int64_t)nt * BLK);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int64_t m = m0 + (wm * 4 + i) * 16 + 4 * ch + e;
-                if (m < a.M)
-                  a.acc_dump[a.M * a.N * G + (e_g * a.M + m) * BLK + rr] = racc[i][e] >> 8;
+                if (m < a.M) a.acc_dump[a.M * a.N * G + (e_g * a.M + m) * BLK + rr] = acc[i][e] >> 8;
               }
-            }
           }
         }
       }
     }
   };
 
-  unsigned char* st0 = smem;
-  unsigned char* st1 = smem + STAGE;
-  Stage R0, R1;
+  const uint32_t st = lds_addr(smem);
+  Stage<C::NSR> R0, R1;
   load(R0, 0);
   load(R1, 1);
-  store(st0, R0);
+  store(st, R0);
   load(R0, 2);
   __syncthreads();
-  for (int j = 0; j < G; j += 2) {
-    compute(st0, j);
-    store(st1, R1);   // group j+1
+  // one exit only, so the accumulators need no copies on the back edge
+  int j = 0;
+  for (; j + 1 < G; j += 2) {
+    compute(st, j);
+    __syncthreads();
+    store(st, R1);  // group j+1
     load(R1, j + 3);
     __syncthreads();
-    if (j + 1 >= G) break;
-    compute(st1, j + 1);
-    store(st0, R0);   // group j+2
+    compute(st, j + 1);
+    __syncthreads();
+    store(st, R0);  // group j+2
     load(R0, j + 4);
     __syncthreads();
   }
+  if (j < G) compute(st, j);  // odd group count: the last group
 
-  // ---- output ----
+  // ---- output (the widened codes carry a factor 256) ----
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -314,7 +433,7 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t m = m0 + (wm * 4 + i) * 16 + 4 * ch + e;
-        if (m < a.M && n < a.N) a.y[m * a.ldy + n] = f2h_bits(y[i][q][e]);
+        if (m < a.M && n < a.N) a.y[m * a.ldy + n] = f2h_bits(y[i][q][e] * kInv256);
       }
     }
 }
@@ -322,15 +441,30 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(GemmArgs a) {
 template <int BLK, bool DUMP>
 hipError_t launch_tile_cfg(const GemmArgs& a, hipStream_t st) {
   using C = TileCfg<BLK>;
-  constexpr int SA = 64 * 8 * 16;
-  constexpr int STAGE = 3 * SA + TBM * 4 + TBN * 2 + C::SRS * 2;
-  const size_t lds = 2 * (size_t)STAGE + (size_t)C::NBR * (size_t)(a.K / BLK) * 2;
+  const size_t lds = C::lds(a.K);
+  auto kern = gemm_tile_kernel<BLK, DUMP>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
   const int64_t tiles = ((a.M + TBM - 1) / TBM) * ((a.N + TBN - 1) / TBN);
-  hipLaunchKernelGGL((gemm_tile_kernel<BLK, DUMP>), dim3((unsigned)tiles), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), lds, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
+
+bool tile_gemm_fits(const GemmArgs& a) {
+  const int64_t lim = (int64_t)1 << 32;
+  const int64_t G = a.K / kGroup;
+  if (a.M * (a.K / 2) >= lim || a.N * (a.K / 2) >= lim || a.M * G * 4 >= lim ||
+      (int64_t)a.n_select * a.block * a.block / 2 >= ((int64_t)1 << 31))
+    return false;
+  switch (a.block) {
+    case 32: return TileCfg<32>::lds(a.K) <= kMaxLds;
+    case 64: return TileCfg<64>::lds(a.K) <= kMaxLds;
+    default: return TileCfg<128>::lds(a.K) <= kMaxLds;
+  }
+}
 
 hipError_t launch_tile_gemm(const GemmArgs& a, hipStream_t st) {
   const bool d = a.acc_dump != nullptr;

@@ -94,6 +94,7 @@ struct GemmArgs {
 };
 
 hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st);
+bool tile_gemm_fits(const GemmArgs& a);
 hipError_t launch_tile_gemm(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mq
