@@ -47,30 +47,36 @@ namespace {
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-constexpr int TBM = 128;  // tokens per tile
-constexpr int TBN = 128;  // output channels per tile
-constexpr size_t kMaxLds = 80 * 1024;  // two workgroups per CU
+constexpr int TBM = 256;    // tokens per tile
+constexpr int TBN = 128;    // output channels per tile
+constexpr int NTHR = 512;   // eight waves: 4 (tokens) x 2 (channels), 64 x 64 each
+constexpr size_t kMaxLds = 160 * 1024;
 
 template <int BLK>
 struct TileCfg {
-  static constexpr int NBR = TBN / BLK;                // block rows in a tile
-  static constexpr int NBC = kGroup / BLK;             // block columns in a group
-  static constexpr int NSR = (TBN * NBC + 255) / 256;  // residual-scale loads per thread
-  static constexpr int SRS = NSR * 256;                // residual-scale slots per stage
-  static constexpr int OPB = 8 * 2 * 64 * 16;          // bytes of one widened operand tile
-  static constexpr int STAGE = 3 * OPB + (TBM + TBN + SRS) * 16;
-  static size_t lds(int64_t K) { return (size_t)STAGE + (size_t)NBR * (size_t)(K / BLK) * 2; }
+  static constexpr int NBR = TBN / BLK;      // block rows in a tile
+  static constexpr int NBC = kGroup / BLK;   // block columns in a group
+  static constexpr int NSRS = TBN * NBC;     // residual-scale slots (<= NTHR)
+  static constexpr int OPA = 16 * 2 * 1024;  // widened activation operands (16 row tiles)
+  static constexpr int OPB = 8 * 2 * 1024;   // widened weight / residual operands (8 column tiles)
+  static constexpr int A_OFF = 0;
+  static constexpr int B_OFF = OPA;
+  static constexpr int R_OFF = OPA + OPB;
+  static constexpr int SA_OFF = OPA + 2 * OPB;
+  static constexpr int SW_OFF = SA_OFF + TBM * 16;
+  static constexpr int SR_OFF = SW_OFF + TBN * 16;
+  static constexpr int STAGE = SR_OFF + NSRS * 16;
+  static size_t lds(int64_t K) { return 2 * (size_t)STAGE + (size_t)NBR * (size_t)(K / BLK) * 2; }
 };
 
 // Register buffer of one group.  Residual pieces and scales of blocks that
-// are not selected are loaded from a dummy address; compute reads the
-// residual operand and scale of a block column only when the block is
+// are not selected are loaded from offset 0 of a valid buffer; compute reads
+// the residual operand and scale of a block column only when the block is
 // selected, so that data is never used and needs no mask.
-template <int NSR>
 struct Stage {
-  uint4 A[2], B[2], R[2];
-  uint32_t sc;       // activation scale bits (waves 0-1) or weight scale bits (waves 2-3)
-  uint32_t sr[NSR];  // residual row scale bits
+  uint4 A[2], B, R;
+  uint32_t sc;  // activation scale bits (waves 0-3) or weight scale bits (waves 4-5)
+  uint32_t sr;  // residual row scale bits
 };
 
 // LDS access through 32-bit LDS addresses, so that constant offsets fold
@@ -124,17 +130,17 @@ __device__ __forceinline__ uint4 channel_scale_slot(uint16_t hbits) {
 }
 
 template <int BLK, bool DUMP>
-__global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
+__global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
   using C = TileCfg<BLK>;
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = (int)(a.K / kGroup);
   const int KT = (int)(a.K / BLK);
-  uint16_t* tab = reinterpret_cast<uint16_t*>(smem + C::STAGE);  // [NBR][KT]: entry-rp+1, 0 = none
+  uint16_t* tab = reinterpret_cast<uint16_t*>(smem + 2 * C::STAGE);  // [NBR][KT]: entry-rp+1, 0 = none
   __shared__ int rp_row[C::NBR];
 
   const int tid = threadIdx.x;
-  // (& 3 makes the range known, so LDS offsets fold into the instructions)
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 3;
+  // (& 7 makes the range known, so LDS offsets fold into the instructions)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;
   const int lane = tid & 63;
   const int r16 = lane & 15;
   const int ch = lane >> 4;
@@ -153,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   const int nrows_b = (int)(a.N / BLK);
 
   // ---- entry table of the tile's block rows: tab[rb][kt] ----
-  for (int i = tid; i < C::NBR * KT; i += 256) tab[i] = 0;
+  for (int i = tid; i < C::NBR * KT; i += NTHR) tab[i] = 0;
   if (tid < C::NBR) {
     int r0 = 0;
     if (a.n_select > 0 && nt0 + tid < nrows_b) r0 = min(max(a.row_ptr[nt0 + tid], 0), a.n_select);
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
       if (nt0 + rb >= nrows_b) break;
       const int b0 = rp_row[rb];
       const int b1 = min(max(a.row_ptr[nt0 + rb + 1], b0), a.n_select);
-      for (int e = b0 + tid; e < b1 && e - b0 < 0xFFFF; e += 256) {
+      for (int e = b0 + tid; e < b1 && e - b0 < 0xFFFF; e += NTHR) {
         const int kt = a.col_idx[e];
         if (kt >= 0 && kt < KT) tab[rb * KT + kt] = (uint16_t)(e - b0 + 1);
       }
@@ -175,6 +181,8 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   __syncthreads();
 
   // ---- staging: global -> registers (fixed load count) ----
+  // Lane l of a wave handles row l%16 of a 16-row slab and 16-byte piece
+  // l/16, so the 16 lanes of a piece write 256 consecutive LDS bytes.
   // Per-thread offsets are fixed for the whole K loop; each group adds a
   // uniform step to a uniform base (32-bit offsets: the host routes
   // operands of 4 GiB or more to the streaming kernel).  Pieces and scales
@@ -182,87 +190,74 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   const uint8_t* rbase = a.n_select > 0 ? a.qr : a.qw;
   const uint8_t* sbase = a.n_select > 0 ? reinterpret_cast<const uint8_t*>(a.sr)
                                         : reinterpret_cast<const uint8_t*>(a.sw);
-  uint32_t offA[2], offB[2];
-  int tabR[2], baseR[2];
+  uint32_t offA[2], slotA[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int r = 16 * (wave + 4 * i) + r16, p = ch;  // row, 16-byte piece
-    const int64_t m = min(m0 + r, a.M - 1);
+    const int r = 16 * (wave + 8 * i) + r16;  // token row in the tile
+    offA[i] = (uint32_t)(min(m0 + r, a.M - 1) * Kh + ch * 16);
+    slotA[i] = (uint32_t)((((r >> 4) * 2 + (ch >> 1)) * 64 + r16 + 32 * (ch & 1)) * 16);
+  }
+  const int rw = 16 * wave + r16;  // channel row in the tile
+  const int64_t nw = min(n0 + rw, a.N - 1);
+  const uint32_t offB = (uint32_t)(nw * Kh + ch * 16);
+  const uint32_t slotB = (uint32_t)((((rw >> 4) * 2 + (ch >> 1)) * 64 + r16 + 32 * (ch & 1)) * 16);
+  const int rbw = (int)(nw / BLK) - nt0;
+  const int tabR = rbw * KT + (ch * 32) / BLK;
+  const int baseR = (rp_row[rbw] - 1) * (BLK * BLK / 2) + (int)(nw - (int64_t)(nt0 + rbw) * BLK) * (BLK / 2) +
+                    ((ch * 32) % BLK) / 2;
+  int tabS, baseS;
+  {
+    const int r = min(tid / C::NBC, TBN - 1), c = tid % C::NBC;
     const int64_t n = min(n0 + r, a.N - 1);
-    offA[i] = (uint32_t)(m * Kh + p * 16);
-    offB[i] = (uint32_t)(n * Kh + p * 16);
     const int rb = (int)(n / BLK) - nt0;
-    tabR[i] = rb * KT + (p * 32) / BLK;
-    baseR[i] = (rp_row[rb] - 1) * (BLK * BLK / 2) + (int)(n - (int64_t)(nt0 + rb) * BLK) * (BLK / 2) +
-               ((p * 32) % BLK) / 2;
+    tabS = tid < C::NSRS ? rb * KT + c : -1;
+    baseS = ((rp_row[rb] - 1) * BLK + (int)(n - (int64_t)(nt0 + rb) * BLK)) * 2;
   }
-  int tabS[C::NSR], baseS[C::NSR];
-#pragma unroll
-  for (int i = 0; i < C::NSR; ++i) {
-    const int idx = tid + 256 * i;
-    const int r = idx / C::NBC, c = idx % C::NBC;
-    const int64_t n = min(n0 + min(r, TBN - 1), a.N - 1);
-    const int rb = (int)(n / BLK) - nt0;
-    tabS[i] = idx < TBN * C::NBC ? rb * KT + c : -1;
-    baseS[i] = ((rp_row[rb] - 1) * BLK + (int)(n - (int64_t)(nt0 + rb) * BLK)) * 2;
-  }
-  const uint32_t offS = wave < 2 ? (uint32_t)(min(m0 + tid, a.M - 1) * G * 4)
-                                 : (uint32_t)(min(n0 + (tid - 128), a.N - 1) * G * 2);
+  const uint32_t offS = wave < 4 ? (uint32_t)(min(m0 + tid, a.M - 1) * G * 4)
+                                 : (uint32_t)(min(n0 + min(tid - 256, TBN - 1), a.N - 1) * G * 2);
 
-  auto load = [&](Stage<C::NSR>& S, int j) {
+  auto load = [&](Stage& S, int j) {
     j = min(j, G - 1);
+    // table entries first (tab is zero-filled, so unguarded reads are safe)
+    const int entR = (int)tab[tabR + j * C::NBC];
+    const int entS = (int)tab[max(tabS, 0) + j * C::NBC];
     const uint8_t* qa_j = a.qa + j * 64;
-    const uint8_t* qw_j = a.qw + j * 64;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      S.A[i] = ld16(qa_j + offA[i]);
-      S.B[i] = ld16(qw_j + offB[i]);
-      const int ent = a.n_select > 0 ? (int)tab[tabR[i] + j * C::NBC] : 0;
-      S.R[i] = ld16(rbase + (uint32_t)(ent > 0 ? ent * (BLK * BLK / 2) + baseR[i] : 0));
-    }
-    if (wave < 2) {
+    S.A[0] = ld16(qa_j + offA[0]);
+    S.A[1] = ld16(qa_j + offA[1]);
+    S.B = ld16(a.qw + j * 64 + offB);
+    if (wave < 4) {
       S.sc = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.sa) + j * 4 + offS);
     } else {
       S.sc = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.sw) + j * 2 + offS);
     }
-#pragma unroll
-    for (int i = 0; i < C::NSR; ++i) {
-      const int ent = (a.n_select > 0 && tabS[i] >= 0) ? (int)tab[tabS[i] + j * C::NBC] : 0;
-      S.sr[i] = *reinterpret_cast<const uint16_t*>(sbase + (uint32_t)(ent > 0 ? ent * (BLK * 2) + baseS[i] : 0));
-    }
+    S.R = ld16(rbase + (uint32_t)(entR > 0 ? entR * (BLK * BLK / 2) + baseR : 0));
+    const int es = tabS >= 0 ? entS : 0;
+    S.sr = *reinterpret_cast<const uint16_t*>(sbase + (uint32_t)(es > 0 ? es * (BLK * 2) + baseS : 0));
   };
 
   // registers -> LDS stage: widened operands in lane order, scale operands
-  uint32_t slotW[2];  // byte offset of this thread's first widened slot, per row slab
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 16 * (wave + 4 * i) + r16, p = ch;  // row, 16-byte piece
-    const int h = p >> 1, c0 = (p & 1) * 2;
-    slotW[i] = (uint32_t)((((r >> 4) * 2 + h) * 64 + (r & 15) + 16 * c0) * 16);
-  }
-  auto store = [&](uint32_t st, const Stage<C::NSR>& S) {
+  auto store = [&](uint32_t st, const Stage& S) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const uint32_t b = st + slotW[i];
+      const uint32_t b = st + C::A_OFF + slotA[i];
       lds_st16(b, widen8(S.A[i].x, S.A[i].y));
       lds_st16(b + 256, widen8(S.A[i].z, S.A[i].w));
-      lds_st16(b + C::OPB, widen8(S.B[i].x, S.B[i].y));
-      lds_st16(b + C::OPB + 256, widen8(S.B[i].z, S.B[i].w));
-      lds_st16(b + 2 * C::OPB, widen8(S.R[i].x, S.R[i].y));
-      lds_st16(b + 2 * C::OPB + 256, widen8(S.R[i].z, S.R[i].w));
     }
-    const uint32_t sl = st + 3 * C::OPB + (uint32_t)tid * 16;
-    if (wave < 2) {
-      lds_st16u(sl, token_scale_slot((m0 + tid < a.M) ? __uint_as_float(S.sc) : 0.f));
-    } else {
-      lds_st16u(sl, channel_scale_slot((uint16_t)S.sc));  // channel slots follow the token slots
+    const uint32_t b = st + C::B_OFF + slotB;
+    lds_st16(b, widen8(S.B.x, S.B.y));
+    lds_st16(b + 256, widen8(S.B.z, S.B.w));
+    lds_st16(b + C::OPB, widen8(S.R.x, S.R.y));
+    lds_st16(b + C::OPB + 256, widen8(S.R.z, S.R.w));
+    if (wave < 4) {
+      lds_st16u(st + C::SA_OFF + (uint32_t)tid * 16,
+                token_scale_slot((m0 + tid < a.M) ? __uint_as_float(S.sc) : 0.f));
+    } else if (wave < 6) {
+      lds_st16u(st + C::SW_OFF + (uint32_t)(tid - 256) * 16, channel_scale_slot((uint16_t)S.sc));
     }
-#pragma unroll
-    for (int i = 0; i < C::NSR; ++i)  // slots past TBN*NBC are padding
-      lds_st16u(sl + (TBM + TBN) * 16 + i * 4096, channel_scale_slot((uint16_t)S.sr[i]));
+    if (tid < C::NSRS) lds_st16u(st + C::SR_OFF + (uint32_t)tid * 16, channel_scale_slot((uint16_t)S.sr));
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;  // 64-row x 64-channel quarter of the tile
   float y[4][4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -277,6 +272,14 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   const uint32_t chan_mask = ch < 2 ? 0xFFFFFFFFu : 0u;
   const uint32_t scale_off = (uint32_t)(ch & 1) * 8;
 
+  // One tile step: its MFMAs first, then the previous tile's epilogue (whose
+  // products finished during the MFMAs), then a fence for the scheduler.
+  auto tile_order = [](bool with_epi) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
+    if (with_epi) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
   auto epi = [](float (&yt)[4], const v4f& P, const v4i& acc) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) yt[e] = fmaf(P[e], (float)acc[e], yt[e]);
@@ -290,18 +293,18 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
   const int tidx = tvalid ? (tnt - nt0) * KT + tc : 0;
 
   auto compute = [&](uint32_t st, int j) {
-    // Lane offsets are recomputed from an opaque copy in every step, so the
-    // per-tile constants fold into the LDS instructions' offset fields
-    // instead of being hoisted out of the loop as one register per tile.
-    // Bases include the wave's tile row / column, so only compile-time
-    // constants remain in the per-tile addresses.
-    uint32_t la = st + (uint32_t)lane * 16u + (uint32_t)wm * 8192u;
-    uint32_t lb = st + C::OPB + (uint32_t)lane * 16u + (uint32_t)wn * 8192u;
-    uint32_t sa_b = st + 3 * C::OPB + (uint32_t)r16 * 16u + scale_off + (uint32_t)wm * 1024u;
-    uint32_t sw_b = st + 3 * C::OPB + TBM * 16 + (uint32_t)r16 * 16u + scale_off + (uint32_t)wn * 1024u;
+    // Bases include the wave's tile row / column and are recomputed from an
+    // opaque copy in every step, so only compile-time constants remain in
+    // the per-tile LDS addresses and fold into the instructions' offsets.
+    uint32_t la = st + C::A_OFF + (uint32_t)lane * 16u + (uint32_t)wm * 8192u;
+    uint32_t lb = st + C::B_OFF + (uint32_t)lane * 16u + (uint32_t)wn * 8192u;
+    uint32_t sa_b = st + C::SA_OFF + (uint32_t)r16 * 16u + scale_off + (uint32_t)wm * 1024u;
+    uint32_t sw_b = st + C::SW_OFF + (uint32_t)r16 * 16u + scale_off + (uint32_t)wn * 1024u;
     asm volatile("" : "+v"(la), "+v"(lb), "+v"(sa_b), "+v"(sw_b));
-    int ent_l = 0;
-    if (a.n_select > 0) ent_l = tvalid ? (int)tab[tidx + j * C::NBC] : 0;
+    // tab is zero-filled and always allocated, so the read needs no guard;
+    // the ballot is taken after the first column's tiles, by when it has
+    // arrived
+    const int ent_raw = (int)tab[tidx + j * C::NBC];
     v4i A0[4], A1[4];
     v4s sa_op[4];
 #pragma unroll
@@ -310,7 +313,8 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
       A1[i] = lds_ld16(la + (i * 2 + 1) * 1024);
       sa_op[i] = __builtin_bit_cast(v4s, lds_ld8(sa_b + i * 256));
     }
-    const uint64_t pres = __builtin_amdgcn_ballot_w64(ent_l > 0);
+    int ent_l = 0;
+    uint64_t pres = 0;
     auto chan_op = [&](uint32_t addr) {
       const uint2 v = lds_ld8(addr);
       return __builtin_bit_cast(v4s, make_uint2(v.x & chan_mask, v.y & chan_mask));
@@ -320,8 +324,7 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
     uint2 swn = lds_ld8(sw_b);
     // Per 16-channel column q: the dense tiles run as a two-deep software
     // pipeline (the MFMAs of tile i are issued before the epilogue of tile
-    // i-1), with scheduling barriers so that at most two tiles' products are
-    // live and the accumulators stay in VGPRs.
+    // i-1), so at most two tiles' products are live.
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int tn = wn * 4 + q;
@@ -336,13 +339,17 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
       v4f P[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[i] = mfma(A0[i], B0, zero);
-        acc[i] = mfma(A1[i], B1, acc[i]);
+        const v4i h0 = mfma(A0[i], B0, zero);
         P[i] = mfma_scale(sa_op[i], sw_op);
+        acc[i] = mfma(A1[i], B1, h0);
         if (i > 0) epi(y[i - 1][q], P[i - 1], acc[i - 1]);
-        __builtin_amdgcn_sched_barrier(0);
+        tile_order(i > 0);
       }
       epi(y[3][q], P[3], acc[3]);
+      if (q == 0) {
+        ent_l = tvalid ? ent_raw : 0;
+        pres = __builtin_amdgcn_ballot_w64(ent_l > 0);
+      }
       if (DUMP) {
         const int64_t n = n0 + tn * 16 + r16;
 #pragma unroll
@@ -361,11 +368,11 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
 #pragma unroll
         for (int c = 0; c < C::NBC; ++c) {
           if (!((pres >> (q * C::NBC + c)) & 1u)) continue;
-          // (rare path: the residual bases are formed here)
-          const v4s sr_op = chan_op(st + 3 * C::OPB + (TBM + TBN) * 16 +
-                                    (uint32_t)((tn * 16 + r16) * C::NBC + c) * 16 + scale_off);
-          const v4i R0 = lds_ld16(lb + C::OPB + (q * 2 + 0) * 1024);
-          const v4i R1 = lds_ld16(lb + C::OPB + (q * 2 + 1) * 1024);
+          // (rare path: the residual addresses are formed here)
+          const v4s sr_op = chan_op(st + C::SR_OFF + (uint32_t)((tn * 16 + r16) * C::NBC + c) * 16 + scale_off);
+          const uint32_t lr = st + C::R_OFF + (uint32_t)lane * 16u + (uint32_t)tn * 2048u;
+          const v4i R0 = lds_ld16(lr);
+          const v4i R1 = lds_ld16(lr + 1024);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (BLK == 128) {
@@ -401,28 +408,30 @@ __global__ __launch_bounds__(256, 2) void gemm_tile_kernel(GemmArgs a) {
     }
   };
 
-  const uint32_t st = lds_addr(smem);
-  Stage<C::NSR> R0, R1;
+  // Two LDS stages: group j is computed from stage j%2 while the waves
+  // write group j+1 into the other stage; one barrier per group.  Register
+  // buffers R0/R1 hold groups j+2 and j+3 in flight.
+  const uint32_t st0 = lds_addr(smem);
+  const uint32_t st1 = st0 + C::STAGE;
+  Stage R0, R1;
   load(R0, 0);
   load(R1, 1);
-  store(st, R0);
+  store(st0, R0);
   load(R0, 2);
   __syncthreads();
   // one exit only, so the accumulators need no copies on the back edge
   int j = 0;
   for (; j + 1 < G; j += 2) {
-    compute(st, j);
-    __syncthreads();
-    store(st, R1);  // group j+1
+    compute(st0, j);
+    store(st1, R1);  // group j+1
     load(R1, j + 3);
     __syncthreads();
-    compute(st, j + 1);
-    __syncthreads();
-    store(st, R0);  // group j+2
+    compute(st1, j + 1);
+    store(st0, R0);  // group j+2
     load(R0, j + 4);
     __syncthreads();
   }
-  if (j < G) compute(st, j);  // odd group count: the last group
+  if (j < G) compute(st0, j);  // odd group count: the last group
 
   // ---- output (the widened codes carry a factor 256) ----
 #pragma unroll
@@ -447,7 +456,7 @@ hipError_t launch_tile_cfg(const GemmArgs& a, hipStream_t st) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((a.M + TBM - 1) / TBM) * ((a.N + TBN - 1) / TBN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NTHR), lds, st, a);
   return hipGetLastError();
 }
 
