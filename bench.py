@@ -23,7 +23,6 @@ region measures the GPU, not Python launch overhead (--no-graph: eager).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -77,14 +76,6 @@ def gemm_ops(M, N, K, b, ns):
     return 2 * M * N * K + 2 * M * ns * b * b
 
 
-def kernel_sources_sha() -> str:
-    h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "dense_sparse_w4a4_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
-        h.update(open(os.path.join(csrc, f), "rb").read())
-    return h.hexdigest()[:16]
-
-
 def traffic_from_profile(wname: str):
     """HBM bytes per GEMM launch measured with rocprofv3 counters, if the
     stored measurement was taken on the current kernel sources."""
@@ -92,6 +83,7 @@ def traffic_from_profile(wname: str):
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
+    from dense_sparse_w4a4_amd.profiling import kernel_sources_sha
     if d.get("sources_sha") != kernel_sources_sha():
         return None
     return d.get("bytes_per_launch")
@@ -292,7 +284,8 @@ def main():
         roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_MFMA_PEAK_TOPS,
                     unit="TOP/s", frac=round(achieved / INT8_MFMA_PEAK_TOPS, 4))
     roof["traffic"] = traffic_from_profile(args.workload)
-    roof["kernel"] = "gemm_stream_kernel"
+    # the library runs M <= 32 on the streaming kernel, larger M on the tile kernel
+    roof["kernel"] = "gemm_stream_kernel" if max(M for _, M in pairs) <= 32 else "gemm_tile_kernel"
     roof["avg_launch_us"] = round(gemm_time_s / launches * 1e6, 3)
     roof["alg_bytes_per_launch"] = per_step_gemm_bytes / launches
     roof["alg_ops_per_launch"] = per_step_ops / launches

@@ -1,0 +1,128 @@
+"""Summaries of rocprofv3 output for the fused-layer kernels.
+
+    python -m dense_sparse_w4a4_amd.profiling stats  OUTDIR PREFIX TITLE CMD > summary.md
+    python -m dense_sparse_w4a4_amd.profiling traffic FETCH_DIR WRITE_DIR WORKLOAD KERNEL CMD > traffic.json
+
+`stats` turns a `rocprofv3 --kernel-trace --stats -f csv` output directory
+into a short markdown table (per kernel, and per launch shape of the fused
+GEMM kernels).  `traffic` combines two `rocprofv3 --pmc FETCH_SIZE` /
+`--pmc WRITE_SIZE` runs of `bench.py --copy-calibration` into HBM bytes per
+fused-GEMM launch: each counter is scaled by the ratio of the known bytes of
+the plain device copy in the same run (256 MiB read, 256 MiB written) to
+what the same counter reports for that copy.  The result carries a hash of
+the kernel sources; bench.py reports it only while the sources match.
+"""
+from __future__ import annotations
+
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+COPY_BYTES = 256 << 20
+COPY_KERNEL = "copyBuffer"
+
+
+def kernel_sources_sha() -> str:
+    """Hash of every file under csrc/ (the kernels and their launchers)."""
+    h = hashlib.sha256()
+    csrc = os.path.join(PKG, "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _one(pattern: str) -> str:
+    hits = sorted(glob.glob(pattern))
+    if not hits:
+        raise SystemExit(f"no file matches {pattern}")
+    return hits[0]
+
+
+def _short(name: str) -> str:
+    name = name.replace("mq::(anonymous namespace)::", "").replace("(mq::GemmArgs)", "")
+    return name[:90]
+
+
+def stats(outdir: str, prefix: str, title: str, cmd: str) -> str:
+    rows = list(csv.DictReader(open(_one(os.path.join(outdir, f"{prefix}_kernel_stats.csv")))))
+    trace = list(csv.DictReader(open(_one(os.path.join(outdir, f"{prefix}_kernel_trace.csv")))))
+    out = [f"# {title}", "", "Command (from the repository root on the GPU host):", "", "```", cmd, "```", "",
+           "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---:|---:|---:|---:|---:|"]
+    for r in rows[:12]:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
+    # fused GEMM launches by kernel and grid (the grid identifies the shape)
+    per = defaultdict(list)
+    for t in trace:
+        if "gemm_" in t["Kernel_Name"]:
+            key = (_short(t["Kernel_Name"]), int(t["Grid_Size_X"]), int(t["Workgroup_Size_X"]))
+            per[key].append((int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) / 1e3)
+    if per:
+        out += ["", "Fused GEMM launches by grid:", "", "| kernel | grid (threads) | block | calls | average (us) |",
+                "|---|---:|---:|---:|---:|"]
+        for (k, g, b), v in sorted(per.items()):
+            out.append(f"| `{k}` | {g} | {b} | {len(v)} | {sum(v) / len(v):.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def _counter(path: str, counter: str):
+    per_kernel = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] == counter:
+            per_kernel[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+    return per_kernel
+
+
+def traffic(fetch_dir: str, write_dir: str, workload: str, kernel: str, cmd: str) -> dict:
+    fetch = _counter(_one(os.path.join(fetch_dir, "*counter_collection.csv")), "FETCH_SIZE")
+    write = _counter(_one(os.path.join(write_dir, "*counter_collection.csv")), "WRITE_SIZE")
+
+    def pick(d, sub):
+        vals = [v for k, vs in d.items() if sub in k for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch of a kernel containing '{sub}'")
+        return vals
+
+    # the calibration copy is the largest copyBuffer dispatch
+    fc = max(pick(fetch, COPY_KERNEL))
+    wc = max(pick(write, COPY_KERNEL))
+    f_k = pick(fetch, kernel)
+    w_k = pick(write, kernel)
+    ff = COPY_BYTES / (fc * 1024.0)
+    fw = COPY_BYTES / (wc * 1024.0)
+    fetch_kib = sum(f_k) / len(f_k)
+    write_kib = sum(w_k) / len(w_k)
+    return {
+        "workload": workload,
+        "kernel": kernel,
+        "sources_sha": kernel_sources_sha(),
+        "dispatches": len(f_k),
+        "fetch_kib_per_dispatch": round(fetch_kib, 1),
+        "write_kib_per_dispatch": round(write_kib, 1),
+        "copy_fetch_kib": fc,
+        "copy_write_kib": wc,
+        "fetch_scale": round(ff, 4),
+        "write_scale": round(fw, 4),
+        "bytes_per_launch": round((fetch_kib * ff + write_kib * fw) * 1024.0),
+        "command": cmd,
+    }
+
+
+def main(argv):
+    if len(argv) >= 5 and argv[0] == "stats":
+        sys.stdout.write(stats(argv[1], argv[2], argv[3], argv[4]))
+    elif len(argv) >= 6 and argv[0] == "traffic":
+        json.dump(traffic(argv[1], argv[2], argv[3], argv[4], argv[5]), sys.stdout, indent=1)
+        sys.stdout.write("\n")
+    else:
+        raise SystemExit(__doc__)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
