@@ -21,43 +21,42 @@
 // 16-byte load).  The first 8 bytes feed one MFMA, the last 8 a second, so
 // two MFMAs cover the group.  A residual block (edge b in {32, 64, 128},
 // always inside one group at a 32-aligned offset) covers whole chunks, so its
-// MFMAs reuse the activation registers already loaded for the dense base in
-// the same group (the "zipper"); chunks outside the block feed zeros.
+// MFMAs take the activation fragment of the same group; chunks outside the
+// block feed zeros.
 #include "gemm_common.h"
 
 namespace mq {
 namespace {
 
-
-// Streaming tile for small M: 16 output channels x 16 tokens per workgroup
-// (grid.y walks 16-token tiles).  The KS waves of a workgroup split the K
-// groups into contiguous runs; partial sums are reduced through LDS in wave
-// order.  Activations are the MFMA A operand (rows = tokens), weights the B
-// operand (columns = channels): lane l owns channel n0 + l%16 and tokens
-// 4*(l/16) + i.
+// Streaming kernel for small M (decode): 16 output channels x 16 tokens per
+// workgroup (grid.y walks 16-token tiles).  The KS waves of a workgroup
+// split the K groups into contiguous runs and reduce their partial sums
+// through LDS in wave order.  Activations are the MFMA A operand (rows =
+// tokens), weights the B operand (columns = channels): lane l owns channel
+// n0 + l%16 and tokens 4*(l/16) + i.
 //
-// Each wave consumes one stream of items: first its dense groups, then the
-// residual blocks of its tile row whose block column lies in its groups,
-// then padding.  Every item, dense or residual, is the same work - one
-// 16-byte B fragment (weight or residual codes), one 16-byte A fragment
-// (the activation codes of the item's group), one 2-byte scale (sw[n][j] or
-// sr[e][r]), two MFMAs and a scale-and-add - so the zipper is literally the
-// same instruction stream applied to the residual, against the activation
-// codes of the same group.  Items are processed in units of U, and the next
-// unit's loads are in flight while the current unit computes.  Because every
-// unit issues exactly the same loads (padding items read a cached valid
-// address and are masked to zero), the hardware load counters are waited on
-// exactly, and nothing in the loop depends on the CSR lookup, which is read
-// from a register window only when the stream reaches its residual items.
-template <int BLK, int KS, int U, bool DUMP>
+// The run of dense groups is streamed in units of U groups with two units
+// in flight: the loads of unit t+2 are issued before unit t+1 is computed.
+// Every unit issues the same loads (groups past the run re-read its last
+// group and get scale 0), so the load counters are waited on exactly, and
+// the per-lane offsets are fixed: each unit only moves uniform bases.  The
+// tile's activation and weight scales are staged in LDS once.  The residual
+// blocks of the tile row follow as a second stream with the same item work
+// against the activation fragment of each block's group (the zipper); they
+// are dealt round-robin to the waves, so the waves finish together however
+// the selected blocks cluster in K, and the first one is loaded before the
+// dense stream starts.
+template <int BLK, int KS, bool DUMP>
 __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
+  constexpr int U = 3;
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = (int)(a.K / kGroup);
   float* sa_t = reinterpret_cast<float*>(smem);  // [G][16]: sa/256 of the tile's tokens
-  float* red = reinterpret_cast<float*>(smem);   // [KS][16][17] after the stream
+  float* sw_t = sa_t + G * 16;                     // [G][16]: weight scales of the tile's channels
+  float* red = reinterpret_cast<float*>(smem);   // [KS][16][17] after the streams
 
   // readfirstlane tells the compiler the wave index is uniform, so loop
-  // bounds and item metadata stay scalar
+  // bounds and bases stay scalar
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
@@ -68,226 +67,166 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   const int gb = wave * G / KS;
   const int ng = (wave + 1) * G / KS - gb;
 
-  const uint8_t* wrow = a.qw + (n0 + r16) * Kh + ch * 16;
-  // token rows past M read row M-1 (computed, never stored)
-  const int64_t mr = m0 + r16;
-  const uint8_t* xrow = a.qa + (mr < a.M ? mr : a.M - 1) * Kh + ch * 16;
-  const uint16_t* swrow = a.sw + (n0 + r16) * G;
-
-  // Residual CSR row of this tile (block row nt, block rows rrow .. rrow+15).
-  // Lane l of the window holds the block column of entry wbase + l.
-  const int nt = (int)(n0 / BLK);
-  const int rrow = (int)(n0 - (int64_t)nt * BLK);
-  int rp0 = 0, rp1 = 0;
-  if (a.n_select > 0) {
-    rp0 = a.row_ptr[nt];
-    rp1 = a.row_ptr[nt + 1];
-  }
-  int wbase = 0;
-  int kt_win = 0;
+  // per-lane byte offsets (32-bit: the host keeps N*K/2 and M*K/2 below 2^32)
+  const uint32_t offW = (uint32_t)((n0 + r16) * Kh + ch * 16);
+  const int64_t mr = m0 + r16;  // token rows past M read row M-1 (computed, never stored)
+  const uint32_t offX = (uint32_t)((mr < a.M ? mr : a.M - 1) * Kh + ch * 16);
 
   struct Unit {
-    uint4 A[U];     // B-operand fragments (weights or residual codes)
-    uint4 X[U];     // A-operand fragments (activation codes)
-    uint32_t S[U];  // scale bits (fp16 in the low half)
-    float4 sa[U];   // activation scales of the lane's 4 tokens (from LDS)
-  };
-  struct Meta {
-    int j[U];       // group of the item (for the activation scale)
-    int e[U];       // residual entry, or -1 for a dense item, -2 for padding
-    uint32_t rm[U]; // lane mask for the B fragment
+    uint4 W[U];  // B-operand fragments (weight codes)
+    uint4 X[U];  // A-operand fragments (activation codes)
   };
 
-  // ---- the wave's residual items: [e_first, e_first + nr) ----
-  // Register work only (the window was loaded once in the prologue), so no
-  // load in the stream depends on it.  Entries the single window cannot
-  // show run after the stream (see below).
-  int nr = -1, e_first = rp0;
-  bool window_full = false;
-  auto ensure_nr = [&]() {
-    if (nr >= 0) return;
-    nr = 0;
-    if (rp1 <= rp0 || ng <= 0) return;
-    const int kt0 = gb * kGroup / BLK;
-    const int kt1 = (gb + ng) * kGroup / BLK;
-    const bool valid = wbase + lane < rp1;
-    const int below = __popcll(__ballot(valid && kt_win < kt0));
-    const int inside = __popcll(__ballot(valid && kt_win >= kt0 && kt_win < kt1));
-    e_first = wbase + below;
-    nr = inside;
-    window_full = (below + inside == 64) && (wbase + 64 < rp1);
-  };
-
-  auto item_meta = [&](int i, Meta& M, int u, const uint8_t*& ap, const uint16_t*& sp) {
-    if (i < ng) {
-      const int j = gb + i;
-      M.j[u] = j;
-      M.e[u] = -1;
-      M.rm[u] = 0xFFFFFFFFu;
-      ap = wrow + (int64_t)j * 64;
-      sp = swrow + j;
-    } else if (i < ng + nr) {
-      const int e = e_first + (i - ng);
-      const int kt = __builtin_amdgcn_readlane(kt_win, e - wbase);
-      const int j = kt * BLK / kGroup;
-      const int lo = kt * BLK - j * kGroup;
-      const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK);
-      M.j[u] = j;
-      M.e[u] = e;
-      M.rm[u] = act ? 0xFFFFFFFFu : 0u;
-      ap = a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + r16) * (BLK / 2) + (act ? 16 * ch - lo / 2 : 0);
-      sp = a.sr + (int64_t)e * BLK + rrow + r16;
-    } else {
-      M.j[u] = gb;
-      M.e[u] = -2;
-      M.rm[u] = 0u;
-      ap = wrow;
-      sp = swrow;
-    }
-  };
-
-  // issue the U items of unit t (exactly 3U loads, always)
-  auto fetch = [&](Unit& D, Meta& M, int t) {
-    if ((t + 1) * U > ng) ensure_nr();
+  // dense unit t: groups gb + t*U + u, clamped to the run
+  auto fetch_dense = [&](Unit& D, int t) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint8_t* ap;
-      const uint16_t* sp;
-      item_meta(t * U + u, M, u, ap, sp);
-      D.A[u] = ld16(ap);
-      D.X[u] = ld16(xrow + (int64_t)M.j[u] * 64);
-      D.S[u] = *sp;
+      const int j = gb + min(t * U + u, ng - 1);
+      D.W[u] = ld16(a.qw + (int64_t)j * 64 + offW);
+      D.X[u] = ld16(a.qa + (int64_t)j * 64 + offX);
     }
-  };
-  // activation scales of a unit, read from LDS one unit ahead of use
-  auto fetch_sa = [&](Unit& D, const Meta& M) {
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-      D.sa[u] = *reinterpret_cast<const float4*>(sa_t + M.j[u] * 16 + 4 * ch);
   };
 
   float y[4] = {0.f, 0.f, 0.f, 0.f};
   const v4i zero = {0, 0, 0, 0};
 
-  auto compute = [&](const Unit& D, const Meta& M) {
-    const float4* sa4 = D.sa;
-    v4i acc[U];
+  // one item: two MFMAs, then y += (sa/256 * s) * acc for the lane's tokens
+  // (s = the item's weight or residual row scale, 0 for padding)
+  auto item = [&](const uint4& W, const uint4& X, float sc, uint32_t rm, int j, bool valid,
+                  int64_t dump_at, bool dump_res) {
+    v4i acc = mfma(widen8(X.x, X.y), widen8(W.x & rm, W.y & rm), zero);
+    acc = mfma(widen8(X.z, X.w), widen8(W.z & rm, W.w & rm), acc);
+    const float4 s4 = *reinterpret_cast<const float4*>(sa_t + j * 16 + 4 * ch);
+    y[0] = fmaf(s4.x * sc, (float)acc[0], y[0]);
+    y[1] = fmaf(s4.y * sc, (float)acc[1], y[1]);
+    y[2] = fmaf(s4.z * sc, (float)acc[2], y[2]);
+    y[3] = fmaf(s4.w * sc, (float)acc[3], y[3]);
+    if (DUMP && valid) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const uint32_t rm = M.rm[u];
-      acc[u] = mfma(widen8(D.X[u].x, D.X[u].y), widen8(D.A[u].x & rm, D.A[u].y & rm), zero);
-      acc[u] = mfma(widen8(D.X[u].z, D.X[u].w), widen8(D.A[u].z & rm, D.A[u].w & rm), acc[u]);
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float sc = (M.e[u] == -2) ? 0.f : h2f((uint16_t)D.S[u]);
-      y[0] = fmaf(sa4[u].x * sc, (float)acc[u][0], y[0]);
-      y[1] = fmaf(sa4[u].y * sc, (float)acc[u][1], y[1]);
-      y[2] = fmaf(sa4[u].z * sc, (float)acc[u][2], y[2]);
-      y[3] = fmaf(sa4[u].w * sc, (float)acc[u][3], y[3]);
-      if (DUMP && M.e[u] != -2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t m = m0 + 4 * ch + i;
-          if (m < a.M) {
-            if (M.e[u] == -1)
-              a.acc_dump[(m * a.N + n0 + r16) * G + M.j[u]] = acc[u][i] >> 8;
-            else
-              a.acc_dump[a.M * a.N * G + ((int64_t)M.e[u] * a.M + m) * BLK + rrow + r16] =
-                  acc[u][i] >> 8;
-          }
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + 4 * ch + i;
+        if (m < a.M) {
+          if (!dump_res)
+            a.acc_dump[(m * a.N + n0 + r16) * G + j] = acc[i] >> 8;
+          else
+            a.acc_dump[dump_at + m * BLK] = acc[i] >> 8;
         }
       }
     }
   };
-
-  // ---- prologue: unit 0 in flight, then the activation scales to LDS ----
-  Unit U0, U1;
-  Meta M0, M1;
-  // unit 0 holds only dense items unless the wave has fewer than U groups;
-  // in that case the CSR lookup happens first
-  if (ng > 0 && ng >= U) fetch(U0, M0, 0);
-  if (a.n_select > 0) {
-    rp0 = min(max(rp0, 0), a.n_select);
-    rp1 = min(max(rp1, rp0), a.n_select);
-    wbase = rp0;
-    if (rp1 > rp0) kt_win = a.col_idx[min(rp0 + lane, rp1 - 1)];
-  }
-  if (ng > 0 && ng < U) fetch(U0, M0, 0);
-  {
-    const int bd = 64 * KS;
-    for (int i0 = threadIdx.x; i0 < 16 * G; i0 += 4 * bd) {
-      float v[4];
+  auto compute_dense = [&](const Unit& D, int t) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int idx = min(i0 + q * bd, 16 * G - 1);
-        const int mm = idx / G;
-        v[q] = a.sa[(m0 + mm < a.M ? m0 + mm : a.M - 1) * G + (idx - mm * G)];
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int idx = i0 + q * bd;
-        if (idx < 16 * G) {
-          const int mm = idx / G, j = idx - mm * G;
-          sa_t[j * 16 + mm] = (m0 + mm < a.M) ? v[q] * kInv256 : 0.f;
-        }
-      }
+    for (int u = 0; u < U; ++u) {
+      const bool valid = t * U + u < ng;
+      const int j = gb + min(t * U + u, ng - 1);
+      item(D.W[u], D.X[u], valid ? sw_t[j * 16 + r16] : 0.f, 0xFFFFFFFFu, j, valid, 0, false);
     }
+  };
+
+  // ---- prologue: the tile's scale loads first, then two dense units and
+  // the CSR window in flight; the scales go to LDS (transposed to [G][16])
+  // as soon as they arrive, without waiting for the units ----
+  const int nunits = (ng + U - 1) / U;
+  constexpr int SMAX = 4;  // staged scale pairs issued ahead, per thread
+  const int nst = 16 * G;
+  const uint8_t* sa_b = reinterpret_cast<const uint8_t*>(a.sa);
+  const uint8_t* sw_b = reinterpret_cast<const uint8_t*>(a.sw) + n0 * G * 2;
+  float pa[SMAX];
+  uint16_t pw[SMAX];
+#pragma unroll
+  for (int k = 0; k < SMAX; ++k) {
+    const int i = min((int)threadIdx.x + k * 64 * KS, nst - 1);
+    const int mm = i / G, j = i - mm * G;
+    const int64_t m = m0 + mm;
+    pa[k] = *reinterpret_cast<const float*>(sa_b + (uint32_t)(((m < a.M ? m : a.M - 1) * G + j) * 4));
+    pw[k] = *reinterpret_cast<const uint16_t*>(sw_b + (uint32_t)(i * 2));
+  }
+  // (every wave has at least one group: the launcher keeps KS <= G; the
+  // loads are unconditional so the waits for the scales above stay exact)
+  Unit U0, U1;
+  fetch_dense(U0, 0);
+  fetch_dense(U1, 1);
+
+  // Residual CSR row of this tile (block row nt, block rows rrow .. rrow+15).
+  // The CSR arrays are read through the scalar cache (uniform addresses, a
+  // read-only view), so their waits never involve the vector loads in flight.
+  typedef const __attribute__((address_space(4))) int32_t* cint_p;
+  const cint_p rpc = (cint_p)a.row_ptr;
+  const cint_p cic = (cint_p)a.col_idx;
+  const int nt = (int)(n0 / BLK);
+  const int rrow = (int)(n0 - (int64_t)nt * BLK);
+  int rp0 = 0, rp1 = 0;
+  if (a.n_select > 0) {
+    rp0 = min(max(rpc[nt], 0), a.n_select);
+    rp1 = min(max(rpc[nt + 1], rp0), a.n_select);
+  }
+  // this wave's residual entries are rp0 + wave + KS*k (see below); the
+  // first one's block column is fetched now
+  const int nres = rp1 > rp0 ? (rp1 - rp0 - wave + KS - 1) / KS : 0;
+  auto res_kt = [&](int k) { return cic[rp0 + wave + KS * k]; };
+  const int kt_first = nres > 0 ? res_kt(0) : 0;
+  const int kt_second = nres > 1 ? res_kt(1) : 0;
+
+  // (stores past the table go to one spare slot, so no store is branched
+  // and the waits stay exact)
+  auto stage = [&](int i, float v, uint16_t w) {
+    const int mm = i / G, j = i - mm * G;
+    const int slot = i < nst ? j * 16 + mm : 2 * nst;
+    sa_t[slot] = (m0 + mm < a.M) ? v * kInv256 : 0.f;
+    sw_t[slot] = h2f(w);
+  };
+#pragma unroll
+  for (int k = 0; k < SMAX; ++k) stage((int)threadIdx.x + k * 64 * KS, pa[k], pw[k]);
+  for (int i = (int)threadIdx.x + SMAX * 64 * KS; i < nst; i += 64 * KS) {  // long K only
+    const int mm = i / G, j = i - mm * G;
+    const int64_t m = m0 + mm;
+    stage(i, a.sa[(m < a.M ? m : a.M - 1) * G + j], a.sw[(n0 + mm) * G + j]);
   }
   __syncthreads();
 
-  // ---- the stream (ping-pong buffers, never copied while in flight) ----
-  if (ng > 0) {
-    fetch_sa(U0, M0);
-    for (int t = 0;; t += 2) {
-      bool more = (t + 1) * U < ng + max(nr, 0) || (t + 1) * U < ng;
-      if (!more && (t + 1) * U >= ng) {
-        ensure_nr();
-        more = (t + 1) * U < ng + nr;
-      }
-      fetch(U1, M1, t + 1);
-      fetch_sa(U1, M1);
-      compute(U0, M0);
-      if (!more) break;
-      bool more2 = (t + 2) * U < ng + max(nr, 0) || (t + 2) * U < ng;
-      if (!more2 && (t + 2) * U >= ng) {
-        ensure_nr();
-        more2 = (t + 2) * U < ng + nr;
-      }
-      fetch(U0, M0, t + 2);
-      fetch_sa(U0, M0);
-      compute(U1, M1);
-      if (!more2) break;
-    }
+  // ---- residual entries: the tile row's entries are dealt round-robin to
+  // the waves (entry rp0 + wave + KS*i), so every wave gets the same share
+  // whatever the block columns; the reduction below sums them with the
+  // dense partials ----
+  auto res_ptrs = [&](int k, int kt, uint4& W, uint4& X, uint32_t& S, uint32_t& rm, int& j) {
+    const int e = rp0 + wave + KS * k;
+    j = kt * BLK / kGroup;
+    const int lo = kt * BLK - j * kGroup;
+    const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK);
+    rm = act ? 0xFFFFFFFFu : 0u;
+    W = ld16(a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + r16) * (BLK / 2) + (act ? 16 * ch - lo / 2 : 0));
+    X = ld16(a.qa + (int64_t)j * 64 + offX);
+    S = a.sr[(int64_t)e * BLK + rrow + r16];
+  };
+  auto res_item = [&](int k, const uint4& W, const uint4& X, uint32_t S, uint32_t rm, int j) {
+    const int64_t e = rp0 + wave + KS * k;
+    item(W, X, h2f((uint16_t)S), rm, j, true, a.M * a.N * G + e * a.M * BLK + rrow + r16, true);
+  };
+  // the first two entries are loaded now, so they arrive during the dense
+  // stream
+  uint4 W0, X0, W1, X1;
+  uint32_t S0 = 0, S1 = 0, rm0 = 0, rm1 = 0;
+  int j0 = 0, j1 = 0;
+  if (nres > 0) res_ptrs(0, kt_first, W0, X0, S0, rm0, j0);
+  if (nres > 1) res_ptrs(1, kt_second, W1, X1, S1, rm1, j1);
+
+  // ---- dense stream (ping-pong buffers, never copied while in flight) ----
+  for (int t = 0; t < nunits; t += 2) {
+    compute_dense(U0, t);
+    if (t + 2 < nunits) fetch_dense(U0, t + 2);
+    if (t + 1 >= nunits) break;
+    compute_dense(U1, t + 1);
+    if (t + 3 < nunits) fetch_dense(U1, t + 3);
   }
 
-  // ---- residual entries the window did not show (rows with more than 64
-  // entries up to this wave's last block column; rare): one at a time ----
-  if (ng > 0 && window_full) {
-    const int kt0 = gb * kGroup / BLK;
-    const int kt1 = (gb + ng) * kGroup / BLK;
-    for (int e = wbase + 64; e < rp1; ++e) {
-      const int kt = a.col_idx[e];
-      if (kt >= kt1) break;
-      if (kt < kt0) continue;
-      const int j = kt * BLK / kGroup;
-      const int lo = kt * BLK - j * kGroup;
-      const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK);
-      Unit D;
-      Meta M;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        M.j[u] = j;
-        M.e[u] = u == 0 ? e : -2;
-        M.rm[u] = (u == 0 && act) ? 0xFFFFFFFFu : 0u;
-        D.A[u] = ld16(a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + r16) * (BLK / 2) +
-                      (act ? 16 * ch - lo / 2 : 0));
-        D.X[u] = ld16(xrow + (int64_t)j * 64);
-        D.S[u] = a.sr[(int64_t)e * BLK + rrow + r16];
-      }
-      fetch_sa(D, M);
-      compute(D, M);
-    }
+  // ---- residual stream: the same item work against the activation
+  // fragment of each block's group, two entries in flight ----
+  for (int k = 0; k < nres; k += 2) {
+    res_item(k, W0, X0, S0, rm0, j0);
+    if (k + 2 < nres) res_ptrs(k + 2, res_kt(k + 2), W0, X0, S0, rm0, j0);
+    if (k + 1 >= nres) break;
+    res_item(k + 1, W1, X1, S1, rm1, j1);
+    if (k + 3 < nres) res_ptrs(k + 3, res_kt(k + 3), W1, X1, S1, rm1, j1);
   }
 
   __syncthreads();  // scales no longer needed: reuse LDS for the reduction
@@ -304,27 +243,29 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   }
 }
 
-template <int BLK, int KS, int U, bool DUMP>
+template <int BLK, int KS, bool DUMP>
 hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t st) {
   const int64_t G = a.K / kGroup;
-  const size_t stage = (size_t)G * 16 * 4;
+  const size_t stage = (size_t)G * 16 * 4 * 2 + 4 * 16 * 4 + 16;
   const size_t reduce = (size_t)KS * 16 * 17 * 4;
   const size_t lds = stage > reduce ? stage : reduce;
   dim3 grid((unsigned)(a.N / 16), (unsigned)((a.M + 15) / 16));
-  hipLaunchKernelGGL((gemm_stream_kernel<BLK, KS, U, DUMP>), grid, dim3(64 * KS), lds, st, a);
+  hipLaunchKernelGGL((gemm_stream_kernel<BLK, KS, DUMP>), grid, dim3(64 * KS), lds, st, a);
   return hipGetLastError();
 }
 
-// Waves per tile: enough workgroups to fill the machine, at least one unit
-// of items per wave.
+// Waves per tile: the most (up to 16) that keep the grid within one
+// resident round (<= 4096 waves, 16 per CU) and give every wave at least
+// one unit of 4 groups.
 template <int BLK, bool DUMP>
 hipError_t launch_stream(const GemmArgs& a, hipStream_t st) {
   const int64_t G = a.K / kGroup;
   const int64_t tiles = (a.N / 16) * ((a.M + 15) / 16);
-  if (tiles >= 768 && G >= 8) return launch_stream_cfg<BLK, 4, 4, DUMP>(a, st);
-  if (G >= 32) return launch_stream_cfg<BLK, 8, 4, DUMP>(a, st);
-  if (G >= 8) return launch_stream_cfg<BLK, 4, 4, DUMP>(a, st);
-  return launch_stream_cfg<BLK, 2, 4, DUMP>(a, st);
+  if (tiles * 16 <= 4096 && G >= 64) return launch_stream_cfg<BLK, 16, DUMP>(a, st);
+  if (tiles * 8 <= 4096 && G >= 32) return launch_stream_cfg<BLK, 8, DUMP>(a, st);
+  if (tiles * 4 <= 4096 && G >= 16) return launch_stream_cfg<BLK, 4, DUMP>(a, st);
+  if (G >= 8) return launch_stream_cfg<BLK, 2, DUMP>(a, st);
+  return launch_stream_cfg<BLK, 1, DUMP>(a, st);
 }
 
 template <int BLK>
@@ -335,7 +276,7 @@ hipError_t launch_blk(const GemmArgs& a, hipStream_t st) {
 }  // namespace
 
 hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st) {
-  // large M: LDS-tiled MFMA kernel (weights read once per 128-token tile);
+  // large M: LDS-tiled MFMA kernel (weights read once per 256-token tile);
   // small M, or a K too long for the tile kernel's LDS table: the streaming
   // kernel (weights read once per 16-token tile)
   if (a.M > 32 && tile_gemm_fits(a)) return launch_tile_gemm(a, st);
