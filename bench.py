@@ -135,6 +135,72 @@ def cpu_baseline(layers, budget_s: float):
                        f"threads = cores) over {what}")
 
 
+def sweep_llama3_70b(args):
+    """Llama-3-70B FFN (K=8192, N=28672), M=256: fused-GEMM time for every
+    (block edge, budget) pair relative to the same block edge at budget 0,
+    next to the output distortion recovered, 1 - D(S_rho)/D(empty), on the
+    calibration tokens and on held-out tokens from the same generator.
+    Prints one JSON line."""
+    import torch
+    from dense_sparse_w4a4_amd import evaluate, ops
+    from dense_sparse_w4a4_amd import synthetic as syn
+    dev = torch.device("cuda:0")
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
+    M = syn.LLAMA3_70B_M
+    rows = []
+    base = syn.llama3_70b(64, 0.0)
+    w = torch.from_numpy(syn.make_weight(base)).to(dev)
+    xc = torch.from_numpy(syn.make_calib(base)).to(dev)
+    xh = torch.from_numpy(syn.make_acts(base, 512)).to(dev)   # held-out tokens (same layer, other draw)
+    x = torch.from_numpy(syn.make_acts(base, M)).to(dev)
+    qa, sa = ops.quantize_act(x)
+    y = torch.empty((M, base.N), dtype=torch.float16, device=dev)
+    cap = torch.cuda.Stream()
+    for b in syn.LLAMA3_70B_BLOCKS:
+        t_zero = None
+        d0 = {}
+        for rho in syn.LLAMA3_70B_RHOS:
+            spec = syn.llama3_70b(b, rho)
+            sel, _, _ = ops.select_blocks(w, xc, b, spec.n_select)
+            L = ops.pack_weights(w, b, sel)
+            R = max(2, -(-ROTATE_BYTES // L.nbytes()))
+            cs = [L.clone() for _ in range(R)]
+            for c in cs:
+                ops.fused_gemm(qa, sa, c, out=y)
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                for c in cs:
+                    ops.fused_gemm(qa, sa, c, out=y)
+            torch.cuda.synchronize()
+            g.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(args.steps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            t = e0.elapsed_time(e1) * 1e-3 / (args.steps * R)
+            if rho == 0.0:
+                t_zero = t
+                d0 = {k: evaluate.distortion(xe, w, L, with_residual=False) for k, xe in (("calib", xc), ("holdout", xh))}
+            d = {k: evaluate.distortion(xe, w, L) for k, xe in (("calib", xc), ("holdout", xh))}
+            ops_ = gemm_ops(M, spec.N, spec.K, b, spec.n_select)
+            row = dict(block=b, rho=rho, n_select=spec.n_select, us=round(t * 1e6, 2),
+                       time_vs_rho0=round(t / t_zero, 4), tops=round(ops_ / t / 1e12, 1),
+                       recovered_calib=round(1 - d["calib"] / d0["calib"], 4),
+                       recovered_holdout=round(1 - d["holdout"] / d0["holdout"], 4))
+            rows.append(row)
+            log(f"[sweep] b={b:3d} rho={rho:4.2f} n_sel={spec.n_select:6d}: {t * 1e6:8.2f} us "
+                f"(x{t / t_zero:5.3f} vs rho=0)  recovered calib {row['recovered_calib']:.3f} "
+                f"held-out {row['recovered_holdout']:.3f}")
+            del cs, L, g
+            torch.cuda.empty_cache()
+    print(json.dumps({"metric": METRIC, "workload": "llama3-70b-ffn-8192x28672-M256-sweep",
+                      "unit": "us", "data": "synthetic", "n_gpus": 1, "steps": args.steps,
+                      "sweep": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,6 +213,8 @@ def main():
     ap.add_argument("--per-shape", action="store_true", help="also time each (shape, M) on its own")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter calibration)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="Llama-3-70B FFN block-size x budget grid: time vs rho=0 and distortion recovered")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -161,6 +229,10 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.sweep:
+        ops.lib()
+        sweep_llama3_70b(args)
+        return
     dev = torch.device("cuda:0")
     ops.lib()
     layers, bound = workload(args.workload)
@@ -255,24 +327,36 @@ def main():
         gem_ms, _ = timed(args.steps, lambda i: run_set(i, False))
     gemm_time_s = gem_ms * 1e-3 / args.steps  # per step (all pairs)
 
-    # per-(shape, M) launch times, each pair replayed in its own graph
+    # per-(shape, M) launch times, each pair replayed in its own graph, and
+    # the same kernel on a dense-only copy (empty CSR) for the residual cost
+    per_shape = []
     if args.per_shape and use_graph:
-        for p_idx, (spec, M) in enumerate(pairs):
+        def pair_time(p_idx, dense_only):
             gs = []
             for r in range(R):
                 (sp_, M_, L, x, qa, sa, y) = sets[r][p_idx]
+                if dense_only:
+                    L = ops.PackedLayer(L.N, L.K, L.block, L.qw, L.sw, torch.zeros_like(L.row_ptr),
+                                        L.col_idx[:0], L.qr[:0], L.sr[:0])
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
                     for _ in range(8):
                         ops.fused_gemm(qa, sa, L, out=y)
                 gs.append(g)
             t_ms, _ = timed(20, lambda i: gs[i % R].replay())
-            t = t_ms * 1e-3 / (20 * 8)
+            return t_ms * 1e-3 / (20 * 8)
+        for p_idx, (spec, M) in enumerate(pairs):
+            t = pair_time(p_idx, False)
+            t0 = pair_time(p_idx, True)
             gb = gemm_bytes(M, spec.N, spec.K, spec.block, spec.n_select)
             go = gemm_ops(M, spec.N, spec.K, spec.block, spec.n_select)
+            per_shape.append(dict(K=spec.K, N=spec.N, M=M, us=round(t * 1e6, 3), dense_only_us=round(t0 * 1e6, 3),
+                                  residual_cost=round(t / t0 - 1, 4), gbs=round(gb / t / 1e9, 1),
+                                  tops=round(go / t / 1e12, 2)))
             log(f"[bench]   K={spec.K:6d} N={spec.N:6d} M={M:5d}: gemm {t * 1e6:8.2f} us  "
                 f"{gb / t / 1e9:8.1f} GB/s ({gb / t / 1e9 / HBM_PEAK_GBS:5.1%} HBM)  "
-                f"{go / t / 1e12:8.2f} TOPS ({go / t / 1e12 / INT8_MFMA_PEAK_TOPS:5.1%} int8 MFMA)")
+                f"{go / t / 1e12:8.2f} TOPS ({go / t / 1e12 / INT8_MFMA_PEAK_TOPS:5.1%} int8 MFMA)  "
+                f"dense-only {t0 * 1e6:8.2f} us (residual +{t / t0 - 1:5.1%})")
 
     launches = len(pairs)
     if bound == "hbm":
@@ -323,6 +407,8 @@ def main():
         },
         "roofline": roof,
     }
+    if per_shape:
+        out["per_shape"] = per_shape
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
         out["cpu_baseline"] = cpu_baseline(layers, args.cpu_budget)

@@ -136,11 +136,19 @@ mq_status mq_pack_weights(const uint16_t* w, int64_t N, int64_t K, int32_t block
                     "mq_pack_weights launch");
 }
 
+// Split-K partials of the tile kernel: [splits][M][N] fp32 when M > 32 and
+// the tiles alone would leave compute units idle; 0 otherwise.
+static size_t split_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M <= 32 || N <= 0 || K < kGroup) return 0;
+  const int ks = tile_gemm_splits(M, N, K);
+  return ks > 1 ? (size_t)ks * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   g_err[0] = 0;
   MQ_REQUIRE(bytes, MQ_ERR_NULL_PTR, "bytes must be non-NULL");
   MQ_REQUIRE(M >= 0 && N >= 0 && K >= 0, MQ_ERR_SHAPE, "sizes must be >= 0");
-  *bytes = 0;
+  *bytes = split_workspace(M, N, K);
   return MQ_OK;
 }
 
@@ -151,8 +159,6 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
                         size_t workspace_bytes, uint32_t flags, int32_t* acc_dump,
                         void* stream) {
   g_err[0] = 0;
-  (void)workspace;
-  (void)workspace_bytes;
   MQ_REQUIRE((flags & ~MQ_FLAG_DUMP_ACC) == 0, MQ_ERR_ARG, "unknown flags 0x%x", flags);
   MQ_REQUIRE(valid_block(block), MQ_ERR_BLOCK, "block = %d must be 32, 64 or 128", block);
   MQ_REQUIRE(M >= 0, MQ_ERR_SHAPE, "M = %lld must be >= 0", (long long)M);
@@ -165,6 +171,8 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
   MQ_REQUIRE(B < ((int64_t)1 << 31), MQ_ERR_SHAPE, "too many blocks (%lld)", (long long)B);
   MQ_REQUIRE(M < ((int64_t)1 << 31) && N < ((int64_t)1 << 31) && K < ((int64_t)1 << 31),
              MQ_ERR_SHAPE, "sizes must be below 2^31");
+  MQ_REQUIRE(N * (K / 2) < ((int64_t)1 << 32) && M * (K / 2) < ((int64_t)1 << 32), MQ_ERR_SHAPE,
+             "packed weights and activations must each be below 4 GiB");
   MQ_REQUIRE(n_select >= 0 && n_select <= B, MQ_ERR_BUDGET, "n_select = %d outside [0, %lld]",
              n_select, (long long)B);
   if (M == 0) return MQ_OK;
@@ -195,6 +203,11 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
   a.y = y;
   a.ldy = ldy;
   a.acc_dump = (flags & MQ_FLAG_DUMP_ACC) ? acc_dump : nullptr;
+  // split-K only with a large enough workspace; otherwise one pass over K
+  const size_t need = split_workspace(M, N, K);
+  const bool split = need > 0 && workspace && workspace_bytes >= need && aligned16(workspace);
+  a.part = split ? static_cast<float*>(workspace) : nullptr;
+  a.ksplit = split ? tile_gemm_splits(M, N, K) : 1;
   return hip_status(launch_fused_gemm(a, (hipStream_t)stream), "mq_fused_gemm launch");
 }
 

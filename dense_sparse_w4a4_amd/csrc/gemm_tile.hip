@@ -145,13 +145,19 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
   const int r16 = lane & 15;
   const int ch = lane >> 4;
 
-  // XCD-aware tile order: consecutive tiles (same token rows, adjacent
-  // channel tiles) go to the same XCD so its L2 serves the shared A rows.
+  // XCD-aware order: consecutive work items (same K split, same token rows,
+  // adjacent channel tiles) go to the same XCD so its L2 serves the shared
+  // A rows.  With split-K, work item = split * tiles + tile.
   const int tiles_n = (int)((a.N + TBN - 1) / TBN);
-  const int tiles = (int)gridDim.x;
+  const int items = (int)gridDim.x;
+  const int tiles = items / a.ksplit;
   const int xcd = blockIdx.x % 8;
-  const int per = tiles / 8, rem = tiles % 8;
-  const int tile = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + blockIdx.x / 8;
+  const int per = items / 8, rem = items % 8;
+  const int item = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + blockIdx.x / 8;
+  const int split = item / tiles;
+  const int tile = item - split * tiles;
+  const int jb = (int)((int64_t)split * G / a.ksplit);             // this split's groups
+  const int je = (int)((int64_t)(split + 1) * G / a.ksplit);       // [jb, je)
   const int64_t m0 = (int64_t)(tile / tiles_n) * TBM;
   const int64_t n0 = (int64_t)(tile % tiles_n) * TBN;
   const int64_t Kh = a.K / 2;
@@ -217,7 +223,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
                                  : (uint32_t)(min(n0 + min(tid - 256, TBN - 1), a.N - 1) * G * 2);
 
   auto load = [&](Stage& S, int j) {
-    j = min(j, G - 1);
+    j = min(j, je - 1);
     // table entries first (tab is zero-filled, so unguarded reads are safe)
     const int entR = (int)tab[tabR + j * C::NBC];
     const int entS = (int)tab[max(tabS, 0) + j * C::NBC];
@@ -414,14 +420,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
   const uint32_t st0 = lds_addr(smem);
   const uint32_t st1 = st0 + C::STAGE;
   Stage R0, R1;
-  load(R0, 0);
-  load(R1, 1);
+  load(R0, jb);
+  load(R1, jb + 1);
   store(st0, R0);
-  load(R0, 2);
+  load(R0, jb + 2);
   __syncthreads();
   // one exit only, so the accumulators need no copies on the back edge
-  int j = 0;
-  for (; j + 1 < G; j += 2) {
+  int j = jb;
+  for (; j + 1 < je; j += 2) {
     compute(st0, j);
     store(st1, R1);  // group j+1
     load(R1, j + 3);
@@ -431,7 +437,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
     load(R0, j + 4);
     __syncthreads();
   }
-  if (j < G) compute(st0, j);  // odd group count: the last group
+  if (j < je) compute(st0, j);  // odd group count: the last group
 
   // ---- output (the widened codes carry a factor 256) ----
 #pragma unroll
@@ -442,9 +448,26 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int64_t m = m0 + (wm * 4 + i) * 16 + 4 * ch + e;
-        if (m < a.M && n < a.N) a.y[m * a.ldy + n] = f2h_bits(y[i][q][e] * kInv256);
+        if (m < a.M && n < a.N) {
+          if (a.part)
+            a.part[((int64_t)split * a.M + m) * a.N + n] = y[i][q][e] * kInv256;
+          else
+            a.y[m * a.ldy + n] = f2h_bits(y[i][q][e] * kInv256);
+        }
       }
     }
+}
+
+// Split-K reduce: y = fp16(sum of the splits' fp32 partials, in split order),
+// so the result does not depend on the order the workgroups ran in.
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part, int ksplit,
+                                                           int64_t M, int64_t N, uint16_t* y, int64_t ldy) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * N) return;
+  const int64_t m = idx / N, n = idx - m * N;
+  float s = 0.f;
+  for (int k = 0; k < ksplit; ++k) s += part[((int64_t)k * M + m) * N + n];
+  y[m * ldy + n] = f2h_bits(s);
 }
 
 template <int BLK, bool DUMP>
@@ -456,11 +479,28 @@ hipError_t launch_tile_cfg(const GemmArgs& a, hipStream_t st) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((a.M + TBM - 1) / TBM) * ((a.N + TBN - 1) / TBN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)tiles), dim3(NTHR), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * a.ksplit)), dim3(NTHR), lds, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((a.M * a.N + 255) / 256)), dim3(256), 0, st,
+                     a.part, a.ksplit, a.M, a.N, a.y, a.ldy);
   return hipGetLastError();
 }
 
 }  // namespace
+
+// K splits: when the tiles alone leave CUs idle (one 512-thread workgroup
+// per CU), split K so that tiles x splits fills at most one round, keeping
+// at least 8 groups per split.
+int tile_gemm_splits(int64_t M, int64_t N, int64_t K) {
+  constexpr int64_t kCUs = 256;
+  const int64_t tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
+  const int64_t G = K / kGroup;
+  int64_t ks = kCUs / (tiles > 0 ? tiles : 1);
+  ks = ks < 8 ? ks : 8;
+  ks = ks < G / 8 ? ks : G / 8;
+  return ks > 1 ? (int)ks : 1;
+}
 
 bool tile_gemm_fits(const GemmArgs& a) {
   const int64_t lim = (int64_t)1 << 32;

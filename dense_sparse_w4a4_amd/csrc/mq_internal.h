@@ -91,10 +91,13 @@ struct GemmArgs {
   uint16_t* y;
   int64_t ldy;
   int32_t* acc_dump;  // non-null => dump accumulators
+  float* part;        // split-K partial outputs [ksplit][M][N] (tile kernel), or null
+  int ksplit;         // K splits of the tile kernel (1 = none)
 };
 
 hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st);
 bool tile_gemm_fits(const GemmArgs& a);
+int tile_gemm_splits(int64_t M, int64_t N, int64_t K);  // K splits the tile kernel would use
 hipError_t launch_tile_gemm(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mq

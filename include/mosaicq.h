@@ -139,9 +139,11 @@ mq_status mq_pack_weights(const uint16_t* w, int64_t N, int64_t K, int32_t block
 #define MQ_FLAG_DUMP_ACC 1u
 
 /*
- * Bytes of workspace mq_fused_gemm needs for this shape (host output).
- * The current kernels need none; the call exists so callers can size a
- * buffer once and stay compatible with split-K schedules.
+ * Bytes of workspace mq_fused_gemm can use for this shape (host output).
+ * Nonzero only for M > 32 when the 256 x 128 output tiles alone would leave
+ * compute units idle: the K groups are then split over several workgroups,
+ * which write fp32 partial outputs [splits][M][N] into the workspace, and a
+ * second kernel sums them in split order (so y stays deterministic).
  */
 mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes);
 
@@ -164,7 +166,12 @@ mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes
  *              points outside [0, n_select) or past K is clipped, never
  *              read out of bounds (check it with mq_validate_csr).
  *   y        : fp16 [M][ldy], ldy >= N, ldy % 8 == 0 (output)
- *   workspace: may be NULL when mq_fused_gemm_workspace reports 0
+ *   workspace: device buffer of workspace_bytes (16-byte aligned) or NULL.
+ *              With at least mq_fused_gemm_workspace's bytes the split-K
+ *              schedule is used; with less, or NULL, one pass over K (same
+ *              result up to fp32 summation order, slower for such shapes).
+ *              The call owns it until the stream has drained.
+ *   Also:      N*K/2 and M*K/2 must each be below 2^32 (MQ_ERR_SHAPE).
  *   flags    : 0 or MQ_FLAG_DUMP_ACC
  *   acc_dump : with MQ_FLAG_DUMP_ACC, int32 [M*N*(K/128) + n_select*M*block]:
  *              acc_base as [M][N][K/128] followed by acc_res as

@@ -126,6 +126,10 @@ GEMM_CASES = [
     (257, 192, 256, 64, 0.15),
     (64, 128, 1024, 128, 0.25),
     (33, 64, 128, 64, 1.00),
+    # split-K tile schedule (few tiles, long K): fp32 partials + ordered reduce
+    (300, 256, 2048, 64, 0.10),
+    (40, 128, 4096, 128, 0.25),
+    (129, 384, 3072, 32, 0.15),
 ]
 
 
@@ -246,3 +250,30 @@ def test_graph_replay_matches_eager():
         torch.cuda.synchronize()
         assert np.array_equal(host(y).view(np.uint16), ref), f"replay {i} differs"
         del junk
+
+
+def test_split_k_without_workspace_matches():
+    # the same call with the workspace withheld runs one pass over K: the
+    # accumulators are identical and y agrees within the tolerance
+    M, N, K, b = 300, 256, 2048, 64
+    assert ops.fused_gemm_workspace(M, N, K) > 0
+    spec = syn.LayerSpec("s", K=K, N=N, T=32, block=b, rho=0.1)
+    w, xc = _layer(spec, seed=5)
+    x = syn.make_acts(spec, M, seed=6)
+    rsel, _, _ = oracle.select_blocks(w, xc, b, spec.n_select)
+    ref = oracle.pack_weights(w, b, rsel)
+    rqa, rsa = oracle.quantize_act(x)
+    y_ref, _, _ = oracle.fused_gemm(rqa, rsa, ref)
+    layer = ops.PackedLayer(N, K, b, dev(ref["qw"]), dev(ref["sw"]), dev(ref["row_ptr"]),
+                            dev(ref["col_idx"]), dev(ref["qr"]), dev(ref["sr"]))
+    qa, sa = dev(oracle.pack_nibbles(rqa)), dev(rsa)
+    y_split = ops.fused_gemm(qa, sa, layer)
+    y_one = torch.empty_like(y_split)
+    st = ops._check("mq_fused_gemm", ops.lib().mq_fused_gemm(
+        ops._ptr(qa), ops._ptr(sa), M, N, K, ops._ptr(layer.qw), ops._ptr(layer.sw), b,
+        layer.n_select, ops._ptr(layer.row_ptr), ops._ptr(layer.col_idx), ops._ptr(layer.qr),
+        ops._ptr(layer.sr), ops._ptr(y_one), N, None, 0, 0, None, ops._stream(None)))
+    torch.cuda.synchronize()
+    assert st is None
+    assert_y_close(y_split, y_ref)
+    assert_y_close(y_one, y_ref)
