@@ -331,32 +331,39 @@ def main():
     # the same kernel on a dense-only copy (empty CSR) for the residual cost
     per_shape = []
     if args.per_shape and use_graph:
-        def pair_time(p_idx, dense_only):
+        def pair_time(p_idx, mode):
+            # mode: "fused" (the layer), "dense" (same kernel, empty CSR),
+            # "unfused" (dense-only launch + the standalone residual kernel
+            # that reloads the activations and merges into y)
             gs = []
             for r in range(R):
                 (sp_, M_, L, x, qa, sa, y) = sets[r][p_idx]
-                if dense_only:
-                    L = ops.PackedLayer(L.N, L.K, L.block, L.qw, L.sw, torch.zeros_like(L.row_ptr),
-                                        L.col_idx[:0], L.qr[:0], L.sr[:0])
+                D = ops.PackedLayer(L.N, L.K, L.block, L.qw, L.sw, torch.zeros_like(L.row_ptr),
+                                    L.col_idx[:0], L.qr[:0], L.sr[:0])
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
                     for _ in range(8):
-                        ops.fused_gemm(qa, sa, L, out=y)
+                        ops.fused_gemm(qa, sa, L if mode == "fused" else D, out=y)
+                        if mode == "unfused":
+                            ops.residual_merge(qa, sa, L, y)
                 gs.append(g)
             t_ms, _ = timed(20, lambda i: gs[i % R].replay())
             return t_ms * 1e-3 / (20 * 8)
         for p_idx, (spec, M) in enumerate(pairs):
-            t = pair_time(p_idx, False)
-            t0 = pair_time(p_idx, True)
+            t = pair_time(p_idx, "fused")
+            t0 = pair_time(p_idx, "dense")
+            tu = pair_time(p_idx, "unfused")
             gb = gemm_bytes(M, spec.N, spec.K, spec.block, spec.n_select)
             go = gemm_ops(M, spec.N, spec.K, spec.block, spec.n_select)
             per_shape.append(dict(K=spec.K, N=spec.N, M=M, us=round(t * 1e6, 3), dense_only_us=round(t0 * 1e6, 3),
-                                  residual_cost=round(t / t0 - 1, 4), gbs=round(gb / t / 1e9, 1),
+                                  residual_cost=round(t / t0 - 1, 4), unfused_us=round(tu * 1e6, 3),
+                                  unfused_over_fused=round(tu / t, 4), gbs=round(gb / t / 1e9, 1),
                                   tops=round(go / t / 1e12, 2)))
             log(f"[bench]   K={spec.K:6d} N={spec.N:6d} M={M:5d}: gemm {t * 1e6:8.2f} us  "
                 f"{gb / t / 1e9:8.1f} GB/s ({gb / t / 1e9 / HBM_PEAK_GBS:5.1%} HBM)  "
                 f"{go / t / 1e12:8.2f} TOPS ({go / t / 1e12 / INT8_MFMA_PEAK_TOPS:5.1%} int8 MFMA)  "
-                f"dense-only {t0 * 1e6:8.2f} us (residual +{t / t0 - 1:5.1%})")
+                f"dense-only {t0 * 1e6:8.2f} us (residual +{t / t0 - 1:5.1%})  "
+                f"unfused {tu * 1e6:8.2f} us (x{tu / t:5.3f})")
 
     launches = len(pairs)
     if bound == "hbm":

@@ -211,6 +211,48 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
   return hip_status(launch_fused_gemm(a, (hipStream_t)stream), "mq_fused_gemm launch");
 }
 
+mq_status mq_residual_merge(const uint8_t* qa, const float* sa, int64_t M, int64_t N, int64_t K,
+                            int32_t block, int32_t n_select, const int32_t* row_ptr,
+                            const int32_t* col_idx, const uint8_t* qr, const uint16_t* sr,
+                            uint16_t* y, int64_t ldy, void* stream) {
+  g_err[0] = 0;
+  MQ_REQUIRE(valid_block(block), MQ_ERR_BLOCK, "block = %d must be 32, 64 or 128", block);
+  MQ_REQUIRE(M >= 0, MQ_ERR_SHAPE, "M = %lld must be >= 0", (long long)M);
+  MQ_REQUIRE(N > 0 && N % block == 0, MQ_ERR_SHAPE, "N = %lld must be a positive multiple of %d",
+             (long long)N, block);
+  MQ_REQUIRE(K > 0 && K % kGroup == 0, MQ_ERR_SHAPE, "K = %lld must be a positive multiple of 128",
+             (long long)K);
+  MQ_REQUIRE(ldy >= N, MQ_ERR_SHAPE, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
+  const int64_t B = (N / block) * (K / block);
+  MQ_REQUIRE(M < ((int64_t)1 << 31) && N < ((int64_t)1 << 31) && K < ((int64_t)1 << 31) &&
+                 B < ((int64_t)1 << 31),
+             MQ_ERR_SHAPE, "sizes must be below 2^31");
+  MQ_REQUIRE(n_select >= 0 && n_select <= B, MQ_ERR_BUDGET, "n_select = %d outside [0, %lld]",
+             n_select, (long long)B);
+  if (M == 0 || n_select == 0) return MQ_OK;
+  MQ_REQUIRE(qa && sa && y && row_ptr && col_idx && qr && sr, MQ_ERR_NULL_PTR,
+             "qa, sa, y, row_ptr, col_idx, qr and sr must be non-NULL");
+  MQ_REQUIRE(aligned16(qa) && aligned16(sa) && aligned16(y) && aligned16(row_ptr) &&
+                 aligned16(col_idx) && aligned16(qr) && aligned16(sr),
+             MQ_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  GemmArgs a = {};
+  a.qa = qa;
+  a.sa = sa;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.block = block;
+  a.n_select = n_select;
+  a.row_ptr = row_ptr;
+  a.col_idx = col_idx;
+  a.qr = qr;
+  a.sr = sr;
+  a.y = y;
+  a.ldy = ldy;
+  a.ksplit = 1;
+  return hip_status(launch_residual_merge(a, (hipStream_t)stream), "mq_residual_merge launch");
+}
+
 mq_status mq_validate_csr(const int32_t* row_ptr, const int32_t* col_idx, int64_t N, int64_t K,
                           int32_t block, int32_t n_select, void* stream) {
   g_err[0] = 0;

@@ -96,6 +96,7 @@ struct GemmArgs {
 };
 
 hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st);
+hipError_t launch_residual_merge(const GemmArgs& a, hipStream_t st);
 bool tile_gemm_fits(const GemmArgs& a);
 int tile_gemm_splits(int64_t M, int64_t N, int64_t K);  // K splits the tile kernel would use
 hipError_t launch_tile_gemm(const GemmArgs& a, hipStream_t st);

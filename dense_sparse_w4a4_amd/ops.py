@@ -42,6 +42,8 @@ _SIGS = {
                                      _c_i32, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp,
                                      ctypes.c_size_t, ctypes.c_uint32, _vp, _vp]),
     "mq_validate_csr": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i32, _c_i32, _vp]),
+    "mq_residual_merge": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _vp,
+                                         _vp, _vp, _vp, _vp, _c_i64, _vp]),
 }
 
 _lib = None
@@ -236,6 +238,23 @@ def fused_gemm(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer,
     return out
 
 
+def residual_merge(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer, out: torch.Tensor,
+                   stream=None) -> torch.Tensor:
+    """Unfused ablation: out += deq(Qa(X) R^T) by a standalone residual kernel."""
+    _dev(qa, torch.uint8, "qa")
+    _dev(sa, torch.float32, "sa")
+    _dev(out, torch.float16, "out")
+    M = qa.shape[0]
+    N, K, b, ns = layer.N, layer.K, layer.block, layer.n_select
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != M or out.shape[1] != N:
+        raise ValueError("out must be [M, N] with unit column stride")
+    _check("mq_residual_merge", lib().mq_residual_merge(
+        _ptr(qa), _ptr(sa), M, N, K, b, ns, _ptr(layer.row_ptr) if ns else None,
+        _ptr(layer.col_idx) if ns else None, _ptr(layer.qr) if ns else None,
+        _ptr(layer.sr) if ns else None, _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
 def validate_csr(layer: PackedLayer, stream=None) -> None:
     ns = layer.n_select
     _check("mq_validate_csr", lib().mq_validate_csr(
@@ -256,3 +275,4 @@ mq_pack_weights = pack_weights
 mq_fused_gemm = fused_gemm
 mq_fused_gemm_workspace = fused_gemm_workspace
 mq_validate_csr = validate_csr
+mq_residual_merge = residual_merge

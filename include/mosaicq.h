@@ -187,6 +187,23 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
                         uint32_t flags, int32_t* acc_dump, void* stream);
 
 /*
+ * Unfused ablation (measurement only; the layer's path never needs it): the
+ * residual branch as a standalone kernel.  It reloads the activation codes,
+ * computes deq(Qa(X) . R^T) for the selected blocks and merges it into the
+ * dense output already in y:  y = f16(f32(y) + residual).  Run after
+ * mq_fused_gemm with n_select == 0 it reproduces the separate-kernel design
+ * that the fused kernel replaces, so the two can be timed on the same data.
+ * [summary-pt Metodologia 3: a separate sparse kernel would reload the
+ * activations and merge partial outputs.]
+ *   Arguments as for mq_fused_gemm (the residual arrays are required when
+ *   n_select > 0; n_select == 0 enqueues nothing).  y is read and written.
+ */
+mq_status mq_residual_merge(const uint8_t* qa, const float* sa, int64_t M, int64_t N, int64_t K,
+                            int32_t block, int32_t n_select, const int32_t* row_ptr,
+                            const int32_t* col_idx, const uint8_t* qr, const uint16_t* sr,
+                            uint16_t* y, int64_t ldy, void* stream);
+
+/*
  * Synchronous CSR check (copies row_ptr and col_idx to the host and waits
  * for `stream`): row_ptr[0] == 0, non-decreasing, row_ptr[N/block] ==
  * n_select, col_idx strictly ascending within a row and < K/block.

@@ -277,3 +277,35 @@ def test_split_k_without_workspace_matches():
     assert st is None
     assert_y_close(y_split, y_ref)
     assert_y_close(y_one, y_ref)
+
+
+@pytest.mark.parametrize("M,b", [(16, 64), (300, 32), (70, 128)])
+def test_unfused_ablation_matches(M, b):
+    # dense-only fused GEMM followed by the standalone residual kernel gives
+    # the layer output within the tolerance (the merge rounds y to fp16 once
+    # more, which the tolerance covers)
+    N, K = 512, 1024
+    spec = syn.LayerSpec("abl", K=K, N=N, w_outlier_frac=0.01, x_outlier_count=3, T=32,
+                         block=b, rho=0.2)
+    w, xc = _layer(spec, seed=11)
+    x = syn.make_acts(spec, M, seed=12)
+    rsel, _, _ = oracle.select_blocks(w, xc, b, spec.n_select)
+    ref = oracle.pack_weights(w, b, rsel)
+    rqa, rsa = oracle.quantize_act(x)
+    y_ref, _, _ = oracle.fused_gemm(rqa, rsa, ref)
+    layer = ops.PackedLayer(N, K, b, dev(ref["qw"]), dev(ref["sw"]), dev(ref["row_ptr"]),
+                            dev(ref["col_idx"]), dev(ref["qr"]), dev(ref["sr"]))
+    dense = ops.PackedLayer(N, K, b, layer.qw, layer.sw, torch.zeros_like(layer.row_ptr),
+                            layer.col_idx[:0], layer.qr[:0], layer.sr[:0])
+    qa, sa = dev(oracle.pack_nibbles(rqa)), dev(rsa)
+    y = ops.fused_gemm(qa, sa, dense)
+    ops.residual_merge(qa, sa, layer, y)
+    torch.cuda.synchronize()
+    # the unfused design rounds the dense partial to fp16 before the merge:
+    # one more rounding of at most 2^-12 |y_dense| on top of the layer's bound
+    dref = oracle.pack_weights(w, b, rsel[:0])
+    y_dense_ref, _, _ = oracle.fused_gemm(rqa, rsa, dref)
+    yg = host(y).astype(np.float64)
+    rms = float(np.sqrt(np.mean(y_ref * y_ref)))
+    bound = 1e-3 * np.maximum(np.abs(y_ref), rms) + 2.0 ** -12 * np.abs(y_dense_ref)
+    assert np.all(np.abs(yg - y_ref) <= bound)
