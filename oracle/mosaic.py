@@ -23,6 +23,7 @@ __all__ = [
     "pack_nibbles", "unpack_nibbles", "build_csr", "pack_weights", "unpack_packed",
     "gemm_accumulators", "gemm_output", "fused_gemm", "dequant_weight",
     "residual_dense", "distortion", "proxy_distortion", "layer_reference",
+    "select_exact_greedy",
 ]
 
 
@@ -379,3 +380,52 @@ def proxy_distortion(H: np.ndarray, E: np.ndarray, rhat: np.ndarray, selected, b
     """Diagonal-Hessian proxy sum_{n,k} H[k]*(E - R_hat_S)^2 in fp64."""
     rem = np.asarray(E, np.float64) - residual_dense(rhat, selected, b).astype(np.float64)
     return float(np.sum(np.asarray(H, np.float64)[None, :] * rem * rem))
+
+
+# ----------------------------------------------------------------------------
+# Exact-distortion selection (the costly evaluation the Delta-score replaces)
+# ----------------------------------------------------------------------------
+
+def select_exact_greedy(w: np.ndarray, xe: np.ndarray, b: int, n_select: int) -> np.ndarray:
+    """Greedy top-K by exact output distortion, for comparison with Delta.
+
+    [summary-pt] Metodologia 2 and Contribuições 2: the Hessian-guided
+    Delta-score stands in for a costly exact evaluation of output
+    distortion.  This is that evaluation, made selection by selection: at
+    each step, add the block whose candidate residual lowers
+    ||Xe (W - deq Q - R_S)^T||_F^2 the most given the blocks already chosen
+    (ties to the lower id).  Adding block (nt, kt) changes only the outputs
+    of its b channels: out[:, rows] -= Xe[:, cols] @ R_hat_block^T, so the
+    gain of every block is re-evaluated from the current outputs each step.
+    Returns the chosen ids ascending.  fp64 throughout.
+    """
+    w16 = np.asarray(w, np.float16)
+    N, K = w16.shape
+    qw, sw = quantize_base(w16)
+    E = base_error(w16, qw, sw).astype(np.float64)
+    _, _, rhat = residual_all_blocks(E.astype(np.float32), b)
+    X = np.asarray(xe, np.float16).astype(np.float64)
+    out = X @ E.T                                   # [T, N] outputs of the remainder
+    NT, KT = N // b, K // b
+    R = _block_view(np.asarray(rhat, np.float64), b)  # [nt, r, kt, c]
+    chosen = np.zeros(NT * KT, dtype=bool)
+    picks = []
+    for _ in range(n_select):
+        best, best_gain = -1, -np.inf
+        for nt in range(NT):
+            o = out[:, nt * b:(nt + 1) * b]          # [T, b]
+            base = float(np.sum(o * o))
+            for kt in range(KT):
+                bid = nt * KT + kt
+                if chosen[bid]:
+                    continue
+                d = X[:, kt * b:(kt + 1) * b] @ R[nt, :, kt, :].T   # [T, b]
+                o2 = o - d
+                gain = base - float(np.sum(o2 * o2))
+                if gain > best_gain:
+                    best, best_gain = bid, gain
+        nt, kt = divmod(best, KT)
+        out[:, nt * b:(nt + 1) * b] -= X[:, kt * b:(kt + 1) * b] @ R[nt, :, kt, :].T
+        chosen[best] = True
+        picks.append(best)
+    return np.sort(np.asarray(picks, dtype=np.int32))
