@@ -253,6 +253,32 @@ mq_status mq_residual_merge(const uint8_t* qa, const float* sa, int64_t M, int64
   return hip_status(launch_residual_merge(a, (hipStream_t)stream), "mq_residual_merge launch");
 }
 
+mq_status mq_smooth_weights(const uint16_t* x_calib, int64_t T, const uint16_t* w, int64_t N,
+                            int64_t K, float* x_absmax, float* w_absmax, float* scales,
+                            uint16_t* w_out, void* stream) {
+  g_err[0] = 0;
+  MQ_REQUIRE(T >= 1 && N >= 1 && K >= 1, MQ_ERR_SHAPE, "T, N and K must be >= 1");
+  MQ_REQUIRE(N * K < ((int64_t)1 << 40) && T * K < ((int64_t)1 << 40), MQ_ERR_SHAPE, "sizes too large");
+  MQ_REQUIRE(x_calib && w && x_absmax && w_absmax && scales && w_out, MQ_ERR_NULL_PTR,
+             "x_calib, w, x_absmax, w_absmax, scales and w_out must be non-NULL");
+  MQ_REQUIRE((const void*)w_out != (const void*)w, MQ_ERR_ARG, "w_out must not alias w");
+  return hip_status(launch_smooth_weights(x_calib, T, w, N, K, x_absmax, w_absmax, scales, w_out,
+                                          (hipStream_t)stream),
+                    "mq_smooth_weights launch");
+}
+
+mq_status mq_smooth_acts(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                         const float* scales, uint16_t* x_out, void* stream) {
+  g_err[0] = 0;
+  MQ_REQUIRE(M >= 0 && K >= 1, MQ_ERR_SHAPE, "M must be >= 0 and K >= 1");
+  MQ_REQUIRE(ldx >= K, MQ_ERR_SHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  MQ_REQUIRE(M * K < ((int64_t)1 << 40), MQ_ERR_SHAPE, "sizes too large");
+  if (M == 0) return MQ_OK;
+  MQ_REQUIRE(x && scales && x_out, MQ_ERR_NULL_PTR, "x, scales and x_out must be non-NULL");
+  return hip_status(launch_smooth_acts(x, M, K, ldx, scales, x_out, (hipStream_t)stream),
+                    "mq_smooth_acts launch");
+}
+
 mq_status mq_validate_csr(const int32_t* row_ptr, const int32_t* col_idx, int64_t N, int64_t K,
                           int32_t block, int32_t n_select, void* stream) {
   g_err[0] = 0;

@@ -44,6 +44,8 @@ _SIGS = {
     "mq_validate_csr": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i32, _c_i32, _vp]),
     "mq_residual_merge": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _vp,
                                          _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "mq_smooth_weights": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
+    "mq_smooth_acts": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -255,6 +257,36 @@ def residual_merge(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer, out: 
     return out
 
 
+def smooth_weights(x_calib: torch.Tensor, w: torch.Tensor, stream=None):
+    """Outlier migration: -> (scales fp32 [K], migrated w fp16 [N, K], x_absmax, w_absmax)."""
+    _dev(x_calib, torch.float16, "x_calib")
+    _dev(w, torch.float16, "w")
+    x_calib, w = x_calib.contiguous(), w.contiguous()
+    T, K = x_calib.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("x_calib and w must have the same K")
+    f = dict(dtype=torch.float32, device=w.device)
+    ax, aw, s = torch.empty(K, **f), torch.empty(K, **f), torch.empty(K, **f)
+    w_out = torch.empty_like(w)
+    _check("mq_smooth_weights", lib().mq_smooth_weights(
+        _ptr(x_calib), T, _ptr(w), N, K, _ptr(ax), _ptr(aw), _ptr(s), _ptr(w_out), _stream(stream)))
+    return s, w_out, ax, aw
+
+
+def smooth_acts(x: torch.Tensor, scales: torch.Tensor, stream=None) -> torch.Tensor:
+    """Migrated activations x / scales (fp16 [M, K])."""
+    _dev(x, torch.float16, "x")
+    _dev(scales, torch.float32, "scales")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [M, K] with unit column stride")
+    M, K = x.shape
+    out = torch.empty((M, K), dtype=torch.float16, device=x.device)
+    _check("mq_smooth_acts", lib().mq_smooth_acts(
+        _ptr(x), M, K, x.stride(0), _ptr(scales), _ptr(out), _stream(stream)))
+    return out
+
+
 def validate_csr(layer: PackedLayer, stream=None) -> None:
     ns = layer.n_select
     _check("mq_validate_csr", lib().mq_validate_csr(
@@ -276,3 +308,5 @@ mq_fused_gemm = fused_gemm
 mq_fused_gemm_workspace = fused_gemm_workspace
 mq_validate_csr = validate_csr
 mq_residual_merge = residual_merge
+mq_smooth_weights = smooth_weights
+mq_smooth_acts = smooth_acts

@@ -204,6 +204,33 @@ mq_status mq_residual_merge(const uint8_t* qa, const float* sa, int64_t M, int64
                             uint16_t* y, int64_t ldy, void* stream);
 
 /*
+ * Outlier migration before the decomposition (offline), exponent 1/2:
+ *   x_absmax[k] = max_t |x_calib[t][k]|,  w_absmax[k] = max_n |w[n][k]|
+ *   scales[k]   = sqrt(x_absmax[k] / w_absmax[k])   (fp32, IEEE division and
+ *                 square root; 1 where either maximum is 0)
+ *   w_out[n][k] = f16(w[n][k] * scales[k])           (round to nearest even)
+ * so that X' W'^T ~ X W^T with X' = mq_smooth_acts(X).  The migrated w_out
+ * is what mq_select_blocks / mq_pack_weights then decompose.
+ * [summary-pt Metodologia 1: outliers are migrated between activations and
+ * weights before the weight is split into base and residual.]
+ *   x_calib : fp16 [T][K];  w : fp16 [N][K]
+ *   x_absmax, w_absmax, scales : fp32 [K] (outputs)
+ *   w_out   : fp16 [N][K] (output; must not alias w)
+ *   T, N >= 1, K >= 1.
+ */
+mq_status mq_smooth_weights(const uint16_t* x_calib, int64_t T, const uint16_t* w, int64_t N,
+                            int64_t K, float* x_absmax, float* w_absmax, float* scales,
+                            uint16_t* w_out, void* stream);
+
+/*
+ * Migrated activations: x_out[m][k] = f16(x[m][k] / scales[k]).
+ *   x : fp16 [M][ldx] (ldx >= K);  scales : fp32 [K] from mq_smooth_weights
+ *   x_out : fp16 [M][K] (output).  M == 0 enqueues nothing.
+ */
+mq_status mq_smooth_acts(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                         const float* scales, uint16_t* x_out, void* stream);
+
+/*
  * Synchronous CSR check (copies row_ptr and col_idx to the host and waits
  * for `stream`): row_ptr[0] == 0, non-decreasing, row_ptr[N/block] ==
  * n_select, col_idx strictly ascending within a row and < K/block.

@@ -23,7 +23,7 @@ __all__ = [
     "pack_nibbles", "unpack_nibbles", "build_csr", "pack_weights", "unpack_packed",
     "gemm_accumulators", "gemm_output", "fused_gemm", "dequant_weight",
     "residual_dense", "distortion", "proxy_distortion", "layer_reference",
-    "select_exact_greedy",
+    "select_exact_greedy", "smooth_scales", "smooth_weights", "smooth_acts",
 ]
 
 
@@ -429,3 +429,36 @@ def select_exact_greedy(w: np.ndarray, xe: np.ndarray, b: int, n_select: int) ->
         chosen[best] = True
         picks.append(best)
     return np.sort(np.asarray(picks, dtype=np.int32))
+
+
+# ----------------------------------------------------------------------------
+# Outlier migration before the decomposition (SmoothQuant-style)
+# ----------------------------------------------------------------------------
+
+def smooth_scales(xc: np.ndarray, w: np.ndarray) -> np.ndarray:
+    """Per-input-channel migration scales s[k] = sqrt(max_t |Xc[t,k]| / max_n |W[n,k]|).
+
+    [summary-pt] Metodologia 1: outliers are first migrated between
+    activations and weights, then the migrated weight is decomposed into the
+    dense 4-bit base and the sparse residual.  The pages name the step, not
+    the rule; reading: SmoothQuant's balance with exponent 1/2, computed in
+    fp32 (max of |fp16| is exact; IEEE division and square root, each
+    correctly rounded), and s = 1 where either maximum is 0.
+    Returns float32 [K].
+    """
+    ax = np.max(np.abs(np.asarray(xc, np.float16).astype(np.float32)), axis=0)
+    aw = np.max(np.abs(np.asarray(w, np.float16).astype(np.float32)), axis=0)
+    s = np.ones(ax.shape, dtype=np.float32)
+    ok = (ax > 0) & (aw > 0)
+    s[ok] = np.sqrt(ax[ok] / aw[ok], dtype=np.float32)
+    return s
+
+
+def smooth_weights(w: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Migrated weight W'[n,k] = f16(f32(W[n,k]) * s[k])."""
+    return (np.asarray(w, np.float16).astype(np.float32) * np.asarray(s, np.float32)[None, :]).astype(np.float16)
+
+
+def smooth_acts(x: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """Migrated activations X'[t,k] = f16(f32(X[t,k]) / s[k]), so X' W'^T ~ X W^T."""
+    return (np.asarray(x, np.float16).astype(np.float32) / np.asarray(s, np.float32)[None, :]).astype(np.float16)

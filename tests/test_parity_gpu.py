@@ -309,3 +309,24 @@ def test_unfused_ablation_matches(M, b):
     rms = float(np.sqrt(np.mean(y_ref * y_ref)))
     bound = 1e-3 * np.maximum(np.abs(y_ref), rms) + 2.0 ** -12 * np.abs(y_dense_ref)
     assert np.all(np.abs(yg - y_ref) <= bound)
+
+
+def test_smooth_bit_exact():
+    rng = np.random.default_rng(21)
+    K, N, T, M = 1024, 384, 64, 20
+    spec = syn.LayerSpec("sm", K=K, N=N, w_outlier_frac=0.01, T=T, block=64, rho=0.1)
+    w = syn.make_weight(spec)
+    xc = syn.make_calib(spec)
+    x = syn.make_acts(spec, M)
+    xc[:, 7] = 0           # zero calibration column -> s = 1
+    w[:, 9] = 0            # zero weight column -> s = 1
+    w[3, 11] = np.float16(-65504.0)
+    s, w2, ax, aw = ops.smooth_weights(dev(xc), dev(w))
+    x2 = ops.smooth_acts(dev(x), s)
+    rs = oracle.smooth_scales(xc, w)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(s).view(np.uint32), rs.view(np.uint32))
+    assert np.array_equal(host(w2).view(np.uint16), oracle.smooth_weights(w, rs).view(np.uint16))
+    assert np.array_equal(host(x2).view(np.uint16), oracle.smooth_acts(x, rs).view(np.uint16))
+    assert np.array_equal(host(ax), np.abs(xc.astype(np.float32)).max(0))
+    assert np.array_equal(host(aw), np.abs(w.astype(np.float32)).max(0))
