@@ -2,20 +2,25 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is one pass of the online hot path - activation quantisation then
-the fused GEMM - for every (shape, M) of the workload, with inputs resident
-in HBM.  The offline part (Delta-score selection and packing) runs once on
+One step is one pass of the online hot path - fp16 activations to fp16 y
+through mq_fused_layer (activation quantisation and the fused GEMM; one
+kernel for M <= 4, where the GEMM quantises the token tile itself, else the
+act-quant kernel then the fused GEMM) - for every (shape, M) of the
+workload, with inputs resident in HBM.  The offline part (Delta-score selection and packing) runs once on
 the GPU before timing.  Every (shape, M) in a step reads its own copy of the
 packed weights, and whole copies of the step's data rotate between steps so
 the footprint is >= 512 MB: the 256 MB Infinity Cache cannot serve weights
 from a previous launch.
 
 Printed JSON (one line on stdout):
-  value      algorithmic bytes of the step / step time (GB/s), both kernels
+  value      algorithmic bytes of the step (fp16 X, packed layer, fp16 Y of
+             every (shape, M)) / step time (GB/s)
   tops       algorithmic integer ops of the step / step time
   roofline   the fused GEMM (dominant kernel): algorithmic bytes (decode) or
              ops (prefill) per launch / average launch time, from HIP events
-             around K replays of a graph holding only the step's fused GEMMs
+             around K replays of a graph holding only the step's GEMM
+             launches (the one-kernel layer where M <= 4: its bytes count
+             the fp16 activations it reads instead of codes)
 Launches are replayed from HIP graphs (one per rotating set) so the timed
 region measures the GPU, not Python launch overhead (--no-graph: eager).
   cpu_baseline  the CPU oracle (quantise + fused GEMM) on a bounded sample
@@ -61,15 +66,21 @@ def workload(name: str):
     raise SystemExit(f"unknown workload {name}")
 
 
-def gemm_bytes(M, N, K, b, ns):
-    """Compulsory bytes of one fused GEMM call (each byte counted once)."""
+def weight_bytes(N, K, b, ns):
+    """Packed layer: base codes and scales, residual codes and scales, CSR."""
     G = K // 128
-    return (N * K // 2 + 2 * N * G + ns * (b * b // 2 + 2 * b) + 4 * ns + 4 * (N // b + 1)
-            + M * K // 2 + 4 * M * G + 2 * M * N)
+    return N * K // 2 + 2 * N * G + ns * (b * b // 2 + 2 * b) + 4 * ns + 4 * (N // b + 1)
 
 
-def act_bytes(M, K):
-    return 2 * M * K + M * K // 2 + 4 * M * (K // 128)
+def gemm_bytes(M, N, K, b, ns):
+    """Compulsory bytes of one fused GEMM call from activation codes (each
+    byte counted once)."""
+    return weight_bytes(N, K, b, ns) + M * K // 2 + 4 * M * (K // 128) + 2 * M * N
+
+
+def layer_bytes(M, N, K, b, ns):
+    """Compulsory bytes of the online layer from fp16 activations to fp16 y."""
+    return weight_bytes(N, K, b, ns) + 2 * M * K + 2 * M * N
 
 
 def gemm_ops(M, N, K, b, ns):
@@ -119,7 +130,7 @@ def cpu_baseline(layers, budget_s: float):
             qa, sa = oracle.quantize_act(x)
             oracle.fused_gemm(qa, sa, packed)
             tsec += time.perf_counter() - t0
-            tbytes += act_bytes(M, spec.K) + gemm_bytes(M, spec.N, spec.K, spec.block, ns)
+            tbytes += layer_bytes(M, spec.N, spec.K, spec.block, ns)
             tops += gemm_ops(M, spec.N, spec.K, spec.block, ns)
             if passes == 0:
                 partial.append(f"{spec.K}x{spec.N}@M={M}")
@@ -312,31 +323,39 @@ def main():
             for M in ms:
                 L = layer.clone()
                 x = xs[M].clone()
-                qa = torch.empty((M, spec.K // 2), dtype=torch.uint8, device=dev)
-                sa = torch.empty((M, spec.K // 128), dtype=torch.float32, device=dev)
+                qa, sa = ops.quantize_act(x)  # codes for the GEMM-only timing
                 y = torch.empty((M, spec.N), dtype=torch.float16, device=dev)
-                s.append((spec, M, L, x, qa, sa, y))
+                wsb = ops.fused_layer_workspace(M, spec.N, spec.K)
+                ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+                s.append((spec, M, L, x, qa, sa, y, ws))
         sets.append(s)
+    # pairs the layer runs as one kernel (the GEMM quantises the token tile)
+    one_kernel = [ops.fused_layer_workspace(M, s.N, s.K) == 0 for s, M in pairs]
     torch.cuda.synchronize()
     log(f"[bench] workload {args.workload}: {len(pairs)} (shape, M) pairs per step, "
         f"{R} rotating copies x {step_footprint / 2**20:.1f} MiB, setup {time.perf_counter() - t0:.1f}s")
 
-    per_step_bytes = sum(act_bytes(M, s.K) + gemm_bytes(M, s.N, s.K, s.block, s.n_select) for s, M in pairs)
-    per_step_gemm_bytes = sum(gemm_bytes(M, s.N, s.K, s.block, s.n_select) for s, M in pairs)
+    per_step_bytes = sum(layer_bytes(M, s.N, s.K, s.block, s.n_select) for s, M in pairs)
+    per_step_gemm_bytes = sum((layer_bytes if one else gemm_bytes)(M, s.N, s.K, s.block, s.n_select)
+                              for (s, M), one in zip(pairs, one_kernel))
     per_step_ops = sum(gemm_ops(M, s.N, s.K, s.block, s.n_select) for s, M in pairs)
 
-    def run_set(i, with_quant=True):
-        for (spec, M, L, x, qa, sa, y) in sets[i % R]:
-            if with_quant:
-                ops.quantize_act(x, qa, sa)
-            ops.fused_gemm(qa, sa, L, out=y)
+    def run_set(i, whole_layer=True):
+        # whole_layer: the step (mq_fused_layer); otherwise only the GEMM
+        # launches (the one-kernel layer where it applies, else the fused
+        # GEMM from precomputed codes)
+        for p_idx, (spec, M, L, x, qa, sa, y, ws) in enumerate(sets[i % R]):
+            if whole_layer or one_kernel[p_idx]:
+                ops.fused_layer(x, L, out=y, workspace=ws)
+            else:
+                ops.fused_gemm(qa, sa, L, out=y)
 
     for i in range(max(args.warmup, R)):
         run_set(i)
     torch.cuda.synchronize()
 
-    # One HIP graph per rotating set: the whole step (act-quant + fused GEMM
-    # for every (shape, M)), and the fused GEMMs alone for per-launch timing.
+    # One HIP graph per rotating set: the whole step (the layer for every
+    # (shape, M)), and the GEMM launches alone for per-launch timing.
     use_graph = not args.no_graph
     if use_graph:
         g_step, g_gemm = [], []
@@ -384,18 +403,27 @@ def main():
     per_shape = []
     if args.per_shape and use_graph:
         def pair_time(p_idx, mode):
-            # mode: "fused" (the layer), "dense" (same kernel, empty CSR),
-            # "unfused" (dense-only launch + the standalone residual kernel
-            # that reloads the activations and merges into y)
+            # mode: "fused" (fused GEMM from codes), "dense" (same kernel,
+            # empty CSR), "unfused" (dense-only launch + the standalone
+            # residual kernel that reloads the activations and merges into
+            # y), "layer" (mq_fused_layer from fp16 X), "two" (act-quant
+            # kernel then the fused GEMM)
             gs = []
             for r in range(R):
-                (sp_, M_, L, x, qa, sa, y) = sets[r][p_idx]
+                (sp_, M_, L, x, qa, sa, y, ws) = sets[r][p_idx]
                 D = ops.PackedLayer(L.N, L.K, L.block, L.qw, L.sw, torch.zeros_like(L.row_ptr),
                                     L.col_idx[:0], L.qr[:0], L.sr[:0])
+                q2, s2 = torch.empty_like(qa), torch.empty_like(sa)
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
                     for _ in range(8):
-                        ops.fused_gemm(qa, sa, L if mode == "fused" else D, out=y)
+                        if mode == "layer":
+                            ops.fused_layer(x, L, out=y, workspace=ws)
+                        elif mode == "two":
+                            ops.quantize_act(x, q2, s2)
+                            ops.fused_gemm(q2, s2, L, out=y)
+                        else:
+                            ops.fused_gemm(qa, sa, L if mode == "fused" else D, out=y)
                         if mode == "unfused":
                             ops.residual_merge(qa, sa, L, y)
                 gs.append(g)
@@ -405,17 +433,24 @@ def main():
             t = pair_time(p_idx, "fused")
             t0 = pair_time(p_idx, "dense")
             tu = pair_time(p_idx, "unfused")
+            tl = pair_time(p_idx, "layer")
+            t2 = pair_time(p_idx, "two")
             gb = gemm_bytes(M, spec.N, spec.K, spec.block, spec.n_select)
+            lb = layer_bytes(M, spec.N, spec.K, spec.block, spec.n_select)
             go = gemm_ops(M, spec.N, spec.K, spec.block, spec.n_select)
             per_shape.append(dict(K=spec.K, N=spec.N, M=M, us=round(t * 1e6, 3), dense_only_us=round(t0 * 1e6, 3),
                                   residual_cost=round(t / t0 - 1, 4), unfused_us=round(tu * 1e6, 3),
                                   unfused_over_fused=round(tu / t, 4), gbs=round(gb / t / 1e9, 1),
-                                  tops=round(go / t / 1e12, 2)))
+                                  tops=round(go / t / 1e12, 2), layer_us=round(tl * 1e6, 3),
+                                  layer_one_kernel=bool(one_kernel[p_idx]),
+                                  layer_gbs=round(lb / tl / 1e9, 1), two_kernel_us=round(t2 * 1e6, 3)))
             log(f"[bench]   K={spec.K:6d} N={spec.N:6d} M={M:5d}: gemm {t * 1e6:8.2f} us  "
                 f"{gb / t / 1e9:8.1f} GB/s ({gb / t / 1e9 / HBM_PEAK_GBS:5.1%} HBM)  "
                 f"{go / t / 1e12:8.2f} TOPS ({go / t / 1e12 / INT8_MFMA_PEAK_TOPS:5.1%} int8 MFMA)  "
                 f"dense-only {t0 * 1e6:8.2f} us (residual +{t / t0 - 1:5.1%})  "
-                f"unfused {tu * 1e6:8.2f} us (x{tu / t:5.3f})")
+                f"unfused {tu * 1e6:8.2f} us (x{tu / t:5.3f})  "
+                f"layer {tl * 1e6:8.2f} us ({'one kernel' if one_kernel[p_idx] else 'two kernels'}; "
+                f"act-quant + gemm {t2 * 1e6:8.2f} us)")
 
     launches = len(pairs)
     if bound == "hbm":
@@ -429,6 +464,7 @@ def main():
     roof["traffic"] = traffic_from_profile(args.workload)
     # the library runs M <= 32 on the streaming kernel, larger M on the tile kernel
     roof["kernel"] = "gemm_stream_kernel" if max(M for _, M in pairs) <= 32 else "gemm_tile_kernel"
+    roof["launches_quantising_in_kernel"] = int(sum(one_kernel))
     roof["avg_launch_us"] = round(gemm_time_s / launches * 1e6, 3)
     roof["alg_bytes_per_launch"] = per_step_gemm_bytes / launches
     roof["alg_ops_per_launch"] = per_step_ops / launches

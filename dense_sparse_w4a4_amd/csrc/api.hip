@@ -186,7 +186,7 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
                  aligned16(row_ptr) && aligned16(col_idx) && aligned16(qr) && aligned16(sr) &&
                  aligned16(acc_dump),
              MQ_ERR_ALIGN, "device pointers must be 16-byte aligned");
-  GemmArgs a;
+  GemmArgs a = {};
   a.qa = qa;
   a.sa = sa;
   a.M = M;
@@ -209,6 +209,96 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
   a.part = split ? static_cast<float*>(workspace) : nullptr;
   a.ksplit = split ? tile_gemm_splits(M, N, K) : 1;
   return hip_status(launch_fused_gemm(a, (hipStream_t)stream), "mq_fused_gemm launch");
+}
+
+static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace of mq_fused_layer: none when the streaming kernel quantises the
+// activations itself; otherwise the codes and scales of mq_quantize_act,
+// then the fused GEMM's split-K partials.
+static size_t layer_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K < kGroup || stream_quant_fits(M, N, K)) return 0;
+  return round256((size_t)M * (size_t)(K / 2)) + round256((size_t)M * (size_t)(K / kGroup) * 4) +
+         split_workspace(M, N, K);
+}
+
+mq_status mq_fused_layer_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes) {
+  g_err[0] = 0;
+  MQ_REQUIRE(bytes, MQ_ERR_NULL_PTR, "bytes must be non-NULL");
+  MQ_REQUIRE(M >= 0 && N >= 0 && K >= 0, MQ_ERR_SHAPE, "sizes must be >= 0");
+  *bytes = layer_workspace(M, N, K);
+  return MQ_OK;
+}
+
+mq_status mq_fused_layer(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int64_t N,
+                         const uint8_t* qw, const uint16_t* sw, int32_t block, int32_t n_select,
+                         const int32_t* row_ptr, const int32_t* col_idx, const uint8_t* qr,
+                         const uint16_t* sr, uint16_t* y, int64_t ldy, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  MQ_REQUIRE(valid_block(block), MQ_ERR_BLOCK, "block = %d must be 32, 64 or 128", block);
+  MQ_REQUIRE(M >= 0, MQ_ERR_SHAPE, "M = %lld must be >= 0", (long long)M);
+  MQ_REQUIRE(N > 0 && N % block == 0, MQ_ERR_SHAPE, "N = %lld must be a positive multiple of %d",
+             (long long)N, block);
+  MQ_REQUIRE(K > 0 && K % kGroup == 0, MQ_ERR_SHAPE, "K = %lld must be a positive multiple of 128",
+             (long long)K);
+  MQ_REQUIRE(ldx >= K, MQ_ERR_SHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
+  MQ_REQUIRE(ldy >= N, MQ_ERR_SHAPE, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
+  const int64_t B = (N / block) * (K / block);
+  MQ_REQUIRE(B < ((int64_t)1 << 31), MQ_ERR_SHAPE, "too many blocks (%lld)", (long long)B);
+  MQ_REQUIRE(M < ((int64_t)1 << 31) && N < ((int64_t)1 << 31) && K < ((int64_t)1 << 31),
+             MQ_ERR_SHAPE, "sizes must be below 2^31");
+  MQ_REQUIRE(N * (K / 2) < ((int64_t)1 << 32) && M * (K / 2) < ((int64_t)1 << 32), MQ_ERR_SHAPE,
+             "packed weights and activations must each be below 4 GiB");
+  MQ_REQUIRE(n_select >= 0 && n_select <= B, MQ_ERR_BUDGET, "n_select = %d outside [0, %lld]",
+             n_select, (long long)B);
+  if (M == 0) return MQ_OK;
+  MQ_REQUIRE(x && qw && sw && y, MQ_ERR_NULL_PTR, "x, qw, sw and y must be non-NULL");
+  MQ_REQUIRE(n_select == 0 || (row_ptr && col_idx && qr && sr), MQ_ERR_NULL_PTR,
+             "row_ptr, col_idx, qr and sr must be non-NULL when n_select > 0");
+  MQ_REQUIRE(ldx % 8 == 0 && ldy % 8 == 0, MQ_ERR_ALIGN,
+             "ldx = %lld and ldy = %lld must be multiples of 8", (long long)ldx, (long long)ldy);
+  MQ_REQUIRE(aligned16(x) && aligned16(qw) && aligned16(sw) && aligned16(y) &&
+                 aligned16(row_ptr) && aligned16(col_idx) && aligned16(qr) && aligned16(sr) &&
+                 aligned16(workspace),
+             MQ_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = layer_workspace(M, N, K);
+  MQ_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), MQ_ERR_WORKSPACE,
+             "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  GemmArgs a = {};
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.qw = qw;
+  a.sw = sw;
+  a.block = block;
+  a.n_select = n_select;
+  a.row_ptr = n_select ? row_ptr : nullptr;
+  a.col_idx = n_select ? col_idx : nullptr;
+  a.qr = n_select ? qr : nullptr;
+  a.sr = n_select ? sr : nullptr;
+  a.y = y;
+  a.ldy = ldy;
+  a.ksplit = 1;
+  if (need == 0) {  // one kernel: the streaming GEMM quantises the activations itself
+    a.x = x;
+    a.ldx = ldx;
+    return hip_status(launch_fused_gemm(a, (hipStream_t)stream), "mq_fused_layer launch");
+  }
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* qa = ws;
+  float* sa = reinterpret_cast<float*>(ws + round256((size_t)M * (size_t)(K / 2)));
+  const mq_status st = hip_status(launch_act_quant(x, M, K, ldx, qa, sa, (hipStream_t)stream),
+                                  "mq_fused_layer act-quant launch");
+  if (st != MQ_OK) return st;
+  a.qa = qa;
+  a.sa = sa;
+  const size_t split = split_workspace(M, N, K);
+  if (split > 0) {
+    a.part = reinterpret_cast<float*>(ws + need - split);
+    a.ksplit = tile_gemm_splits(M, N, K);
+  }
+  return hip_status(launch_fused_gemm(a, (hipStream_t)stream), "mq_fused_layer launch");
 }
 
 mq_status mq_residual_merge(const uint8_t* qa, const float* sa, int64_t M, int64_t N, int64_t K,

@@ -46,13 +46,30 @@ namespace {
 // are dealt round-robin to the waves, so the waves finish together however
 // the selected blocks cluster in K, and the first one is loaded before the
 // dense stream starts.
-template <int BLK, int KS, bool DUMP>
+//
+// QP > 0 (M <= kStreamQuantRows, one token tile): the activations arrive as
+// fp16 and the workgroup quantises them itself before the streams start (the
+// act-quant stage fused into the GEMM's prologue).  One (token, group) per
+// team of 16 lanes, 8 channels per lane; the scale is the same fp32 amax/7
+// as the standalone act-quant kernel and the codes come from the same
+// quotient (quant4_rcp), so codes, scales and y are identical to the
+// two-kernel path.  QP passes of the teams cover the tile's M x K/128 pairs.  Codes go to LDS rows of K/2 + 64 bytes (the pad puts the
+// rows on different banks) and the A fragments are read from there.  The
+// fp16 loads are issued before the weight stream, so waiting for them never
+// waits on it.
+template <int BLK, int KS, bool DUMP, int QP>
 __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
-  constexpr int U = 3;
+  // groups per unit: four when the units carry only weight codes (the
+  // activation codes are in LDS), else three, which keeps every variant
+  // within 128 VGPRs (16 resident waves per CU, as the launcher assumes)
+  constexpr int U = QP > 0 ? 4 : 3;
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = (int)(a.K / kGroup);
   float* sa_t = reinterpret_cast<float*>(smem);  // [G][16]: sa/256 of the tile's tokens
   float* sw_t = sa_t + G * 16;                     // [G][16]: weight scales of the tile's channels
+  float* spare = sa_t + 32 * G;                    // [2]: target of stores past the tables
+  unsigned char* qa_t = smem + stream_qa_offset(G);  // QP > 0: [M][qrow] activation codes
+  const int qrow = (int)(a.K / 2) + 64;
   float* red = reinterpret_cast<float*>(smem);   // [KS][16][17] after the streams
 
   // readfirstlane tells the compiler the wave index is uniform, so loop
@@ -71,6 +88,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   const uint32_t offW = (uint32_t)((n0 + r16) * Kh + ch * 16);
   const int64_t mr = m0 + r16;  // token rows past M read row M-1 (computed, never stored)
   const uint32_t offX = (uint32_t)((mr < a.M ? mr : a.M - 1) * Kh + ch * 16);
+  const int offXl = (int)((mr < a.M ? mr : a.M - 1) - m0) * qrow + ch * 16;  // QP > 0: in qa_t
+  auto lds_x = [&](int j) { return *reinterpret_cast<const uint4*>(qa_t + offXl + j * 64); };
 
   struct Unit {
     uint4 W[U];  // B-operand fragments (weight codes)
@@ -83,7 +102,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
     for (int u = 0; u < U; ++u) {
       const int j = gb + min(t * U + u, ng - 1);
       D.W[u] = ld16(a.qw + (int64_t)j * 64 + offW);
-      D.X[u] = ld16(a.qa + (int64_t)j * 64 + offX);
+      if constexpr (QP == 0) D.X[u] = ld16(a.qa + (int64_t)j * 64 + offX);
     }
   };
 
@@ -119,7 +138,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
     for (int u = 0; u < U; ++u) {
       const bool valid = t * U + u < ng;
       const int j = gb + min(t * U + u, ng - 1);
-      item(D.W[u], D.X[u], valid ? sw_t[j * 16 + r16] : 0.f, 0xFFFFFFFFu, j, valid, 0, false);
+      item(D.W[u], QP > 0 ? lds_x(j) : D.X[u], valid ? sw_t[j * 16 + r16] : 0.f, 0xFFFFFFFFu, j,
+           valid, 0, false);
     }
   };
 
@@ -127,6 +147,20 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   // the CSR window in flight; the scales go to LDS (transposed to [G][16])
   // as soon as they arrive, without waiting for the units ----
   const int nunits = (ng + U - 1) / U;
+  // QP > 0: the fp16 activations of the tile's (token, group) pairs, one
+  // 16-byte load per pass and lane, all issued first (the launcher picks QP
+  // so that the passes cover every pair)
+  const int team = (int)(threadIdx.x >> 4), tl = (int)(threadIdx.x & 15);
+  const int nrg = QP > 0 ? (int)a.M * G : 0;
+  uint4 xv[QP > 0 ? QP : 1];
+  if constexpr (QP > 0) {
+#pragma unroll
+    for (int it = 0; it < QP; ++it) {
+      const int rg = min(team + it * 4 * KS, nrg - 1);
+      const int row = rg / G, j = rg - row * G;
+      xv[it] = *reinterpret_cast<const uint4*>(a.x + (m0 + row) * a.ldx + j * kGroup + tl * 8);
+    }
+  }
   constexpr int SMAX = 4;  // staged scale pairs issued ahead, per thread
   const int nst = 16 * G;
   const uint8_t* sa_b = reinterpret_cast<const uint8_t*>(a.sa);
@@ -138,7 +172,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
     const int i = min((int)threadIdx.x + k * 64 * KS, nst - 1);
     const int mm = i / G, j = i - mm * G;
     const int64_t m = m0 + mm;
-    pa[k] = *reinterpret_cast<const float*>(sa_b + (uint32_t)(((m < a.M ? m : a.M - 1) * G + j) * 4));
+    if constexpr (QP == 0)
+      pa[k] = *reinterpret_cast<const float*>(sa_b + (uint32_t)(((m < a.M ? m : a.M - 1) * G + j) * 4));
+    else
+      pa[k] = 0.f;
     pw[k] = *reinterpret_cast<const uint16_t*>(sw_b + (uint32_t)(i * 2));
   }
   // (every wave has at least one group: the launcher keeps KS <= G; the
@@ -167,49 +204,84 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   const int kt_first = nres > 0 ? res_kt(0) : 0;
   const int kt_second = nres > 1 ? res_kt(1) : 0;
 
-  // (stores past the table go to one spare slot, so no store is branched
-  // and the waits stay exact)
+  // ---- residual entries: the tile row's entries are dealt round-robin to
+  // the waves (entry rp0 + wave + KS*i), so every wave gets the same share
+  // whatever the block columns; the reduction below sums them with the
+  // dense partials.  The first two entries' loads are issued whether or not
+  // the wave has them (past its last entry they read valid dummy addresses:
+  // weight codes and scales), so the prologue's load counters are waited on
+  // exactly; later entries are loaded only when they exist, so no load is
+  // left in flight at the end ----
+  auto res_ptrs = [&](int k, int kt, uint4& W, uint4& X, uint32_t& S, uint32_t& rm, int& j) {
+    const bool has = k < nres;
+    const int e = has ? rp0 + wave + KS * k : 0;
+    j = kt * BLK / kGroup;
+    const int lo = kt * BLK - j * kGroup;
+    const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK);
+    rm = act ? 0xFFFFFFFFu : 0u;
+    W = ld16(has ? a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + r16) * (BLK / 2) + (act ? 16 * ch - lo / 2 : 0)
+                 : a.qw + offW);
+    if constexpr (QP == 0) X = ld16(a.qa + (int64_t)j * 64 + offX);
+    S = *(has ? a.sr + (int64_t)e * BLK + rrow + r16 : a.sw);
+  };
+  // the first two entries are loaded now, before the scale staging, so they
+  // arrive during the dense stream
+  uint4 W0, X0, W1, X1;
+  uint32_t S0 = 0, S1 = 0, rm0 = 0, rm1 = 0;
+  int j0 = 0, j1 = 0;
+  res_ptrs(0, kt_first, W0, X0, S0, rm0, j0);
+  res_ptrs(1, kt_second, W1, X1, S1, rm1, j1);
+
+  // (stores past the tables go to the spare slots, so no store is branched
+  // and the waits stay exact; with QP > 0 the activation scales of the
+  // tile's tokens come from the quantisation below and only the padding
+  // rows are written here)
   auto stage = [&](int i, float v, uint16_t w) {
     const int mm = i / G, j = i - mm * G;
-    const int slot = i < nst ? j * 16 + mm : 2 * nst;
-    sa_t[slot] = (m0 + mm < a.M) ? v * kInv256 : 0.f;
-    sw_t[slot] = h2f(w);
+    const bool in = i < nst;
+    const bool pad = m0 + mm >= a.M;
+    float* const da = in && (QP == 0 || pad) ? sa_t + j * 16 + mm : spare;
+    float* const dw = in ? sw_t + j * 16 + mm : spare + 1;
+    *da = pad ? 0.f : v * kInv256;
+    *dw = h2f(w);
   };
 #pragma unroll
   for (int k = 0; k < SMAX; ++k) stage((int)threadIdx.x + k * 64 * KS, pa[k], pw[k]);
   for (int i = (int)threadIdx.x + SMAX * 64 * KS; i < nst; i += 64 * KS) {  // long K only
     const int mm = i / G, j = i - mm * G;
     const int64_t m = m0 + mm;
-    stage(i, a.sa[(m < a.M ? m : a.M - 1) * G + j], a.sw[(n0 + mm) * G + j]);
+    stage(i, QP == 0 ? a.sa[(m < a.M ? m : a.M - 1) * G + j] : 0.f, a.sw[(n0 + mm) * G + j]);
+  }
+  if constexpr (QP > 0) {
+    // quantise the tile: pass it covers pairs team + it * (4 KS), clamped
+    // to the last pair, so every pass is branch-free and teams past the end
+    // rewrite the last pair's codes and scale with identical values
+#pragma unroll
+    for (int it = 0; it < QP; ++it) {
+      const int rg = min(team + it * 4 * KS, nrg - 1);
+      const int row = rg / G, j = rg - row * G;
+      float f[8];
+      unpack_h8(xv[it], f);
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = row16_max(amax);
+      const float s = amax / 7.0f;
+      const float r = s == 0.0f ? 0.0f : 1.0f / s;
+      int q[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) q[i] = quant4_rcp(f[i], s, r);
+      *reinterpret_cast<uint32_t*>(qa_t + row * qrow + j * 64 + tl * 4) = pack8(q);
+      if (tl == 0) sa_t[j * 16 + row] = s * kInv256;
+    }
   }
   __syncthreads();
 
-  // ---- residual entries: the tile row's entries are dealt round-robin to
-  // the waves (entry rp0 + wave + KS*i), so every wave gets the same share
-  // whatever the block columns; the reduction below sums them with the
-  // dense partials ----
-  auto res_ptrs = [&](int k, int kt, uint4& W, uint4& X, uint32_t& S, uint32_t& rm, int& j) {
-    const int e = rp0 + wave + KS * k;
-    j = kt * BLK / kGroup;
-    const int lo = kt * BLK - j * kGroup;
-    const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK);
-    rm = act ? 0xFFFFFFFFu : 0u;
-    W = ld16(a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + r16) * (BLK / 2) + (act ? 16 * ch - lo / 2 : 0));
-    X = ld16(a.qa + (int64_t)j * 64 + offX);
-    S = a.sr[(int64_t)e * BLK + rrow + r16];
-  };
   auto res_item = [&](int k, const uint4& W, const uint4& X, uint32_t S, uint32_t rm, int j) {
     const int64_t e = rp0 + wave + KS * k;
-    item(W, X, h2f((uint16_t)S), rm, j, true, a.M * a.N * G + e * a.M * BLK + rrow + r16, true);
+    item(W, QP > 0 ? lds_x(j) : X, h2f((uint16_t)S), rm, j, true,
+         a.M * a.N * G + e * a.M * BLK + rrow + r16, true);
   };
-  // the first two entries are loaded now, so they arrive during the dense
-  // stream
-  uint4 W0, X0, W1, X1;
-  uint32_t S0 = 0, S1 = 0, rm0 = 0, rm1 = 0;
-  int j0 = 0, j1 = 0;
-  if (nres > 0) res_ptrs(0, kt_first, W0, X0, S0, rm0, j0);
-  if (nres > 1) res_ptrs(1, kt_second, W1, X1, S1, rm1, j1);
-
   // ---- dense stream (ping-pong buffers, never copied while in flight) ----
   for (int t = 0; t < nunits; t += 2) {
     compute_dense(U0, t);
@@ -243,43 +315,91 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   }
 }
 
-template <int BLK, int KS, bool DUMP>
+template <int BLK, int KS, bool DUMP, int QP>
 hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t st) {
-  const int64_t G = a.K / kGroup;
-  const size_t stage = (size_t)G * 16 * 4 * 2 + 4 * 16 * 4 + 16;
-  const size_t reduce = (size_t)KS * 16 * 17 * 4;
-  const size_t lds = stage > reduce ? stage : reduce;
+  const size_t lds = stream_lds_bytes(a.K, KS, QP > 0 ? (int)a.M : 0);
+  if (lds > 64 * 1024) {
+    auto k = gemm_stream_kernel<BLK, KS, DUMP, QP>;
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
   dim3 grid((unsigned)(a.N / 16), (unsigned)((a.M + 15) / 16));
-  hipLaunchKernelGGL((gemm_stream_kernel<BLK, KS, DUMP>), grid, dim3(64 * KS), lds, st, a);
+  hipLaunchKernelGGL((gemm_stream_kernel<BLK, KS, DUMP, QP>), grid, dim3(64 * KS), lds, st, a);
   return hipGetLastError();
+}
+
+template <int BLK, int KS>
+hipError_t launch_stream_ks(const GemmArgs& a, hipStream_t st) {
+  if (a.x) {
+    switch (stream_quant_passes(a.M, a.K, KS)) {
+      case 1: return launch_stream_cfg<BLK, KS, false, 1>(a, st);
+      case 2: return launch_stream_cfg<BLK, KS, false, 2>(a, st);
+      default: return launch_stream_cfg<BLK, KS, false, 4>(a, st);
+    }
+  }
+  return a.acc_dump ? launch_stream_cfg<BLK, KS, true, 0>(a, st) : launch_stream_cfg<BLK, KS, false, 0>(a, st);
+}
+
+template <int BLK>
+hipError_t launch_blk(const GemmArgs& a, hipStream_t st) {
+  switch (stream_waves(a.M, a.N, a.K)) {
+    case 16: return launch_stream_ks<BLK, 16>(a, st);
+    case 8: return launch_stream_ks<BLK, 8>(a, st);
+    case 4: return launch_stream_ks<BLK, 4>(a, st);
+    case 2: return launch_stream_ks<BLK, 2>(a, st);
+    default: return launch_stream_ks<BLK, 1>(a, st);
+  }
+}
+
+}  // namespace
+
+size_t stream_lds_bytes(int64_t K, int ks, int rows) {
+  const int64_t G = K / kGroup;
+  const size_t stage = (size_t)stream_qa_offset((int)G) + (size_t)rows * (size_t)(K / 2 + 64);
+  const size_t reduce = (size_t)ks * 16 * 17 * 4;
+  return stage > reduce ? stage : reduce;
 }
 
 // Waves per tile: the most (up to 16) that keep the grid within one
 // resident round (<= 4096 waves, 16 per CU) and give every wave at least
 // one unit of 4 groups.
-template <int BLK, bool DUMP>
-hipError_t launch_stream(const GemmArgs& a, hipStream_t st) {
-  const int64_t G = a.K / kGroup;
-  const int64_t tiles = (a.N / 16) * ((a.M + 15) / 16);
-  if (tiles * 16 <= 4096 && G >= 64) return launch_stream_cfg<BLK, 16, DUMP>(a, st);
-  if (tiles * 8 <= 4096 && G >= 32) return launch_stream_cfg<BLK, 8, DUMP>(a, st);
-  if (tiles * 4 <= 4096 && G >= 16) return launch_stream_cfg<BLK, 4, DUMP>(a, st);
-  if (G >= 8) return launch_stream_cfg<BLK, 2, DUMP>(a, st);
-  return launch_stream_cfg<BLK, 1, DUMP>(a, st);
+int stream_waves(int64_t M, int64_t N, int64_t K) {
+  const int64_t G = K / kGroup;
+  const int64_t tiles = (N / 16) * ((M + 15) / 16);
+  if (tiles * 16 <= 4096 && G >= 64) return 16;
+  if (tiles * 8 <= 4096 && G >= 32) return 8;
+  if (tiles * 4 <= 4096 && G >= 16) return 4;
+  if (G >= 8) return 2;
+  return 1;
 }
 
-template <int BLK>
-hipError_t launch_blk(const GemmArgs& a, hipStream_t st) {
-  return a.acc_dump ? launch_stream<BLK, true>(a, st) : launch_stream<BLK, false>(a, st);
+// Passes of the in-prologue quantisation: the power of two (<= 4) that
+// covers the tile's M x K/128 (token, group) pairs with the workgroup's
+// 4 * ks teams; 0 if 4 passes do not.  Every workgroup quantises the whole
+// token tile, so the prologue's cost grows with the passes while the launch
+// it saves does not: past 4 passes (measured on the Llama-3-8B and
+// Qwen3-32B decode shapes) the two-kernel route is faster.
+int stream_quant_passes(int64_t M, int64_t K, int ks) {
+  const int64_t pairs = M * (K / kGroup);
+  for (int p = 1; p <= 4; p *= 2)
+    if (pairs <= (int64_t)p * 4 * ks) return p;
+  return 0;
 }
 
-}  // namespace
+bool stream_quant_fits(int64_t M, int64_t N, int64_t K) {
+  if (M < 1 || M > kStreamQuantRows) return false;
+  const int ks = stream_waves(M, N, K);
+  return stream_quant_passes(M, K, ks) > 0 && stream_lds_bytes(K, ks, (int)M) <= 64 * 1024;
+}
 
 hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st) {
-  // large M: LDS-tiled MFMA kernel (weights read once per 256-token tile);
-  // small M, or a K too long for the tile kernel's LDS table: the streaming
-  // kernel (weights read once per 16-token tile)
-  if (a.M > 32 && tile_gemm_fits(a)) return launch_tile_gemm(a, st);
+  // fp16 activations (a.x): the streaming kernel quantises them itself (the
+  // caller checked stream_quant_fits).  Otherwise, large M: LDS-tiled MFMA
+  // kernel (weights read once per 256-token tile); small M, or a K too long
+  // for the tile kernel's LDS table: the streaming kernel (weights read once
+  // per 16-token tile)
+  if (!a.x && a.M > 32 && tile_gemm_fits(a)) return launch_tile_gemm(a, st);
   switch (a.block) {
     case 32: return launch_blk<32>(a, st);
     case 64: return launch_blk<64>(a, st);

@@ -36,6 +36,32 @@ __device__ __forceinline__ int quant4(float v, float s) {
   return (int)r;
 }
 
+// The same code from the reciprocal r = 1/s (r = 0 when s = 0): q0 = v*r,
+// e = v - q0*s (one fma, exact), q1 = q0 + e*r (one fma), which is the
+// correctly rounded quotient v/s (Markstein's correction).  An exhaustive
+// check over every fp16 v and every scale s = amax/7 with fp16 amax >= |v|
+// finds q1 equal to the IEEE quotient except for the sign of a zero
+// quotient, so the codes equal quant4's; three operations per code instead
+// of a full division.
+__device__ __forceinline__ int quant4_rcp(float v, float s, float r) {
+  const float q0 = v * r;
+  const float e = fmaf(-q0, s, v);
+  const float q1 = fmaf(e, r, q0);
+  return (int)fminf(fmaxf(rintf(q1), -7.0f), 7.0f);
+}
+
+// Max over each row of 16 lanes (DPP: swap neighbours, swap pairs, mirror
+// within 8, mirror within 16), for non-negative floats, whose bit patterns
+// order like their values.  Every lane of the row must be active.
+__device__ __forceinline__ float row16_max(float v) {
+  int b = __float_as_int(v);
+  b = max(b, __builtin_amdgcn_update_dpp(b, b, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  b = max(b, __builtin_amdgcn_update_dpp(b, b, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  b = max(b, __builtin_amdgcn_update_dpp(b, b, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  b = max(b, __builtin_amdgcn_update_dpp(b, b, 0x140, 0xF, 0xF, false));  // row_mirror
+  return __int_as_float(b);
+}
+
 // Two codes per byte along K, low nibble first, two's complement.
 __device__ __forceinline__ uint32_t pack8(const int q[8]) {
   uint32_t w = 0;
@@ -93,7 +119,21 @@ struct GemmArgs {
   int32_t* acc_dump;  // non-null => dump accumulators
   float* part;        // split-K partial outputs [ksplit][M][N] (tile kernel), or null
   int ksplit;         // K splits of the tile kernel (1 = none)
+  const uint16_t* x;  // fp16 activations [M][ldx] to quantise in the streaming
+  int64_t ldx;        // kernel (qa, sa unused), or null
 };
+
+// In-kernel activation quantisation of the streaming kernel: at most
+// kStreamQuantRows tokens, and every (token, group) pair of the tile within
+// 4 passes of the workgroup's 16-lane teams.
+constexpr int kStreamQuantRows = 4;
+// LDS byte offset of the streaming kernel's activation codes: after the
+// [G][16] activation and weight scale tables and two spare slots.
+__host__ __device__ constexpr int stream_qa_offset(int G) { return 128 * G + 16; }
+int stream_waves(int64_t M, int64_t N, int64_t K);
+int stream_quant_passes(int64_t M, int64_t K, int ks);
+bool stream_quant_fits(int64_t M, int64_t N, int64_t K);
+size_t stream_lds_bytes(int64_t K, int ks, int rows);
 
 hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st);
 hipError_t launch_residual_merge(const GemmArgs& a, hipStream_t st);

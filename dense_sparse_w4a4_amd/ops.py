@@ -41,6 +41,11 @@ _SIGS = {
     "mq_fused_gemm": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i32,
                                      _c_i32, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp,
                                      ctypes.c_size_t, ctypes.c_uint32, _vp, _vp]),
+    "mq_fused_layer_workspace": (ctypes.c_int, [_c_i64, _c_i64, _c_i64,
+                                                ctypes.POINTER(ctypes.c_size_t)]),
+    "mq_fused_layer": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i32,
+                                      _c_i32, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp,
+                                      ctypes.c_size_t, _vp]),
     "mq_validate_csr": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i32, _c_i32, _vp]),
     "mq_residual_merge": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32, _vp,
                                          _vp, _vp, _vp, _vp, _c_i64, _vp]),
@@ -240,6 +245,41 @@ def fused_gemm(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer,
     return out
 
 
+def fused_layer_workspace(M: int, N: int, K: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("mq_fused_layer_workspace", lib().mq_fused_layer_workspace(M, N, K, ctypes.byref(n)))
+    return int(n.value)
+
+
+def fused_layer(x: torch.Tensor, layer: PackedLayer, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Y fp16 [M, N] from fp16 activations: Qa(X) and the fused GEMM, as one
+    kernel for decode-sized M (the GEMM quantises the token tile itself), or
+    the two kernels through the workspace otherwise.  Same result as
+    fused_gemm(*quantize_act(x), layer)."""
+    _dev(x, torch.float16, "x")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [M, K] with unit column stride")
+    M, K = x.shape
+    N, b, ns = layer.N, layer.block, layer.n_select
+    if K != layer.K:
+        raise ValueError("x must match the layer's K")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=x.device)
+    _dev(out, torch.float16, "out")
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != M or out.shape[1] != N:
+        raise ValueError("out must be [M, N] with unit column stride")
+    wsb = fused_layer_workspace(M, N, K)
+    if wsb and (workspace is None or workspace.numel() * workspace.element_size() < wsb):
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+    _check("mq_fused_layer", lib().mq_fused_layer(
+        _ptr(x), M, K, x.stride(0), N, _ptr(layer.qw), _ptr(layer.sw), b, ns,
+        _ptr(layer.row_ptr) if ns else None, _ptr(layer.col_idx) if ns else None,
+        _ptr(layer.qr) if ns else None, _ptr(layer.sr) if ns else None,
+        _ptr(out), out.stride(0), _ptr(workspace) if wsb else None, wsb, _stream(stream)))
+    return out
+
+
 def residual_merge(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer, out: torch.Tensor,
                    stream=None) -> torch.Tensor:
     """Unfused ablation: out += deq(Qa(X) R^T) by a standalone residual kernel."""
@@ -306,6 +346,8 @@ mq_select_blocks = select_blocks
 mq_pack_weights = pack_weights
 mq_fused_gemm = fused_gemm
 mq_fused_gemm_workspace = fused_gemm_workspace
+mq_fused_layer = fused_layer
+mq_fused_layer_workspace = fused_layer_workspace
 mq_validate_csr = validate_csr
 mq_residual_merge = residual_merge
 mq_smooth_weights = smooth_weights

@@ -187,6 +187,40 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
                         uint32_t flags, int32_t* acc_dump, void* stream);
 
 /*
+ * Bytes of workspace mq_fused_layer needs for this shape (host output).
+ * 0 when the decode kernel quantises the activations itself (M <= 4 and the
+ * shape's (token, group) pairs fit its prologue); otherwise room for the
+ * codes and scales of mq_quantize_act plus mq_fused_gemm_workspace's bytes.
+ */
+mq_status mq_fused_layer_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes);
+
+/*
+ * The whole online layer from fp16 activations: y = mq_fused_gemm applied
+ * to mq_quantize_act(x), with results identical to calling the two (same
+ * codes, same scales, same y bits).  For M <= 4 (decode), when the shape
+ * allows, it is ONE kernel: the streaming GEMM quantises the token tile in
+ * its prologue into LDS and never writes codes to memory, which removes the
+ * separate launch and the codes' round trip through memory; otherwise the
+ * two kernels run back to back on `stream` using the workspace.
+ * [summary-pt Metodologia 3: quantisation is one of the stages the fused
+ * pipeline overlaps with the GEMM.]
+ *   x        : fp16 [M][ldx], ldx >= K, ldx % 8 == 0, finite values
+ *   qw .. sr : the packed layer, as for mq_fused_gemm
+ *   y        : fp16 [M][ldy], ldy >= N, ldy % 8 == 0 (output)
+ *   workspace: device buffer (16-byte aligned) of at least
+ *              mq_fused_layer_workspace's bytes (NULL when that is 0);
+ *              fewer bytes give MQ_ERR_WORKSPACE.  The call owns it until
+ *              the stream has drained.
+ *   M >= 0 (M == 0 enqueues nothing); other constraints as mq_fused_gemm.
+ */
+mq_status mq_fused_layer(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int64_t N,
+                         const uint8_t* qw, const uint16_t* sw,
+                         int32_t block, int32_t n_select, const int32_t* row_ptr,
+                         const int32_t* col_idx, const uint8_t* qr, const uint16_t* sr,
+                         uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,
+                         void* stream);
+
+/*
  * Unfused ablation (measurement only; the layer's path never needs it): the
  * residual branch as a standalone kernel.  It reloads the activation codes,
  * computes deq(Qa(X) . R^T) for the selected blocks and merges it into the

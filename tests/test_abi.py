@@ -133,3 +133,37 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(ops, "_lib", None)
     with pytest.raises(RuntimeError, match="missing"):
         ops.lib()
+
+
+def _layer_call(L, **kw):
+    a = dict(x=P, M=4, K=512, ldx=512, N=512, qw=P, sw=P, b=64, ns=6, rp=P, ci=P, qr=P, sr=P,
+             y=P, ldy=512, ws=None, wsb=0)
+    a.update(kw)
+    return L.mq_fused_layer(a["x"], a["M"], a["K"], a["ldx"], a["N"], a["qw"], a["sw"], a["b"],
+                            a["ns"], a["rp"], a["ci"], a["qr"], a["sr"], a["y"], a["ldy"], a["ws"],
+                            a["wsb"], None)
+
+
+def test_fused_layer_workspace_and_validation(L):
+    n = ctypes.c_size_t(123)
+    # decode-sized token tiles are quantised inside the GEMM: no workspace
+    for M in (1, 4):
+        assert L.mq_fused_layer_workspace(M, 4096, 4096, ctypes.byref(n)) == OK
+        assert n.value == 0
+    # otherwise codes [M][K/2] and scales [M][K/128] fp32, each rounded up to 256 bytes
+    assert L.mq_fused_layer_workspace(16, 4096, 4096, ctypes.byref(n)) == OK
+    assert n.value == 16 * 2048 + 16 * 32 * 4
+    assert L.mq_fused_layer_workspace(5, 512, 640, ctypes.byref(n)) == OK
+    assert n.value == 1792 + 256
+    assert L.mq_fused_layer_workspace(4, 4096, 4096, None) == NULLP
+    assert _layer_call(L, b=100) == BLOCK
+    assert _layer_call(L, ldx=256) == SHAPE
+    assert _layer_call(L, ldy=256) == SHAPE
+    assert _layer_call(L, K=500) == SHAPE
+    assert _layer_call(L, ns=65) == BUDGET
+    assert _layer_call(L, x=None) == NULLP
+    assert _layer_call(L, ldx=516) == ALIGN
+    assert _layer_call(L, x=PMIS) == ALIGN
+    assert _layer_call(L, M=16) == WS                     # two-kernel route needs the workspace
+    assert _layer_call(L, M=16, ws=P, wsb=16 * 256 + 16 * 4 * 4 - 1) == WS
+    assert _layer_call(L, M=0, x=None, y=None) == OK      # empty batch
