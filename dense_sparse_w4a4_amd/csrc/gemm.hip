@@ -85,7 +85,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   const int ng = (wave + 1) * G / KS - gb;
 
   // per-lane byte offsets (32-bit: the host keeps N*K/2 and M*K/2 below 2^32)
-  const uint32_t offW = (uint32_t)((n0 + r16) * Kh + ch * 16);
+  // weight codes in the slab layout: the tile is one 16-channel slab and
+  // each group of it is 1 KB, lane l's 16 bytes at l*16, so every weight
+  // load of a wave reads 1 KB contiguous
+  const uint32_t offW = (uint32_t)(n0 * Kh + lane * 16);
   const int64_t mr = m0 + r16;  // token rows past M read row M-1 (computed, never stored)
   const uint32_t offX = (uint32_t)((mr < a.M ? mr : a.M - 1) * Kh + ch * 16);
   const int offXl = (int)((mr < a.M ? mr : a.M - 1) - m0) * qrow + ch * 16;  // QP > 0: in qa_t
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = gb + min(t * U + u, ng - 1);
-      D.W[u] = ld16(a.qw + (int64_t)j * 64 + offW);
+      D.W[u] = ld16(a.qw + (int64_t)j * 1024 + offW);
       if constexpr (QP == 0) D.X[u] = ld16(a.qa + (int64_t)j * 64 + offX);
     }
   };

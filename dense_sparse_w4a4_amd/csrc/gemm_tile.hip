@@ -205,7 +205,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
   }
   const int rw = 16 * wave + r16;  // channel row in the tile
   const int64_t nw = min(n0 + rw, a.N - 1);
-  const uint32_t offB = (uint32_t)(nw * Kh + ch * 16);
+  // weight codes in the slab layout: wave w stages slab n0/16 + w (the last
+  // slab for tiles past N), 1 KB per group with lane l's bytes at l*16
+  const int64_t slab = min(n0 / 16 + wave, a.N / 16 - 1);
+  const uint32_t offB = (uint32_t)(slab * 16 * Kh + lane * 16);
   const uint32_t slotB = (uint32_t)((((rw >> 4) * 2 + (ch >> 1)) * 64 + r16 + 32 * (ch & 1)) * 16);
   const int rbw = (int)(nw / BLK) - nt0;
   const int tabR = rbw * KT + (ch * 32) / BLK;
@@ -230,7 +233,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
     const uint8_t* qa_j = a.qa + j * 64;
     S.A[0] = ld16(qa_j + offA[0]);
     S.A[1] = ld16(qa_j + offA[1]);
-    S.B = ld16(a.qw + j * 64 + offB);
+    S.B = ld16(a.qw + j * 1024 + offB);
     if (wave < 4) {
       S.sc = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.sa) + j * 4 + offS);
     } else {

@@ -32,7 +32,10 @@ __global__ __launch_bounds__(256) void base_pack_kernel(const uint16_t* __restri
   int q[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) q[i] = quant4(f[i], s);
-  *reinterpret_cast<uint32_t*>(qw + n * (K / 2) + j * (kGroup / 2) + t * 4) = pack8(q);
+  // slab layout: 16-channel slab n/16, group j, lane 16*(t/4) + n%16,
+  // bytes 4*(t%4) .. +3 of that lane's 16
+  *reinterpret_cast<uint32_t*>(qw + (n >> 4) * 8 * K + j * 1024 + ((t >> 2) * 16 + (n & 15)) * 16 +
+                               (t & 3) * 4) = pack8(q);
   if (t == 0) sw[n * G + j] = sb;
 }
 

@@ -25,9 +25,17 @@ def unpack_codes(p: torch.Tensor) -> torch.Tensor:
     return torch.where(q >= 8, q - 16, q).to(torch.int8)
 
 
+def row_bytes(qw: torch.Tensor) -> torch.Tensor:
+    """Packed base codes from the slab layout [N/16, K/128, 64, 16] (lane
+    l = 16c + r of slab s, group j holds bytes 16c..16c+15 of channel
+    16s + r's 64-byte group) back to row-major uint8 [N, K/2]."""
+    S, G = qw.shape[:2]
+    return qw.reshape(S, G, 4, 16, 16).permute(0, 3, 1, 2, 4).reshape(S * 16, G * 64)
+
+
 def dequant_base(layer) -> torch.Tensor:
     """deq Q(W) as float64 [N, K]."""
-    q = unpack_codes(layer.qw).to(torch.float64)
+    q = unpack_codes(row_bytes(layer.qw)).to(torch.float64)
     s = layer.sw.to(torch.float64).repeat_interleave(GROUP, dim=1)
     return q * s
 

@@ -157,7 +157,7 @@ class PackedLayer:
     N: int
     K: int
     block: int
-    qw: torch.Tensor       # uint8 [N, K/2]
+    qw: torch.Tensor       # uint8 [N/16, K/128, 64, 16] (slab layout)
     sw: torch.Tensor       # fp16  [N, K/128]
     row_ptr: torch.Tensor  # int32 [N/b + 1]
     col_idx: torch.Tensor  # int32 [n_select]
@@ -188,7 +188,7 @@ def pack_weights(w: torch.Tensor, block: int, selected: torch.Tensor, stream=Non
     ns = int(selected.numel())
     dev = w.device
     b = int(block)
-    qw = torch.empty((N, K // 2), dtype=torch.uint8, device=dev)
+    qw = torch.empty((N // 16, K // GROUP, 64, 16), dtype=torch.uint8, device=dev)
     sw = torch.empty((N, K // GROUP), dtype=torch.float16, device=dev)
     row_ptr = torch.empty(N // b + 1 if b else 1, dtype=torch.int32, device=dev)
     col_idx = torch.empty(ns, dtype=torch.int32, device=dev)

@@ -121,7 +121,15 @@ mq_status mq_select_blocks(const uint16_t* w, const uint16_t* x_calib,
  *   selected : int32 [n_select], strictly ascending block ids in range
  *              (as written by mq_select_blocks); other contents give
  *              unspecified residual output but every access stays in bounds
- *   qw       : uint8 [N][K/2]       packed base codes (output)
+ *   qw       : uint8 [N/16][K/128][64][16]  packed base codes in the slab
+ *              layout (output): for the 16 channels 16s .. 16s+15 (slab s),
+ *              group j and lane l = 16c + r (c < 4, r < 16), the 16 bytes at
+ *              [s][j][l] are bytes 16c .. 16c+15 of channel 16s + r's 64
+ *              packed bytes of group j (two codes per byte as above).  A
+ *              permutation of the row-major [N][K/2] bytes inside each slab
+ *              and group, so that one 16-channel x 128-input tile is 1 KB
+ *              contiguous, in the order the kernels' lanes read it.  N is a
+ *              multiple of 16 (block >= 32 divides it).
  *   sw       : fp16  [N][K/128]     base scales (output)
  *   row_ptr  : int32 [N/block + 1]  CSR by output tile row (output)
  *   col_idx  : int32 [n_select]     block column kt, ascending per row (output)

@@ -20,7 +20,8 @@ QMAX = 7
 __all__ = [
     "GROUP", "QMAX", "quant4", "quantize_act", "quantize_base", "base_error",
     "residual_all_blocks", "hdiag", "delta_scores", "select_top", "select_blocks",
-    "pack_nibbles", "unpack_nibbles", "build_csr", "pack_weights", "unpack_packed",
+    "pack_nibbles", "unpack_nibbles", "slab_layout", "row_layout", "build_csr",
+    "pack_weights", "unpack_packed",
     "gemm_accumulators", "gemm_output", "fused_gemm", "dequant_weight",
     "residual_dense", "distortion", "proxy_distortion", "layer_reference",
     "select_exact_greedy", "smooth_scales", "smooth_weights", "smooth_acts",
@@ -230,6 +231,34 @@ def unpack_nibbles(p: np.ndarray) -> np.ndarray:
     return out
 
 
+def slab_layout(rows: np.ndarray) -> np.ndarray:
+    """Packed base codes, row-major uint8 [N, K/2] -> the slab layout uint8
+    [N/16, K/128, 64, 16] the library stores.
+
+    The pages fix no byte layout; this one is the library's contract.  For
+    slab s (channels 16s .. 16s+15), group j and lane l = 16c + r (c < 4,
+    r < 16), entry [s, j, l, :] holds the 16 packed bytes j*64 + 16c ..
+    j*64 + 16c + 15 of channel 16s + r: bytes 16c .. 16c+15 of that
+    channel's 64-byte group.  It is a permutation of the row-major bytes
+    inside each 16-channel slab and group.
+    """
+    rows = np.asarray(rows, dtype=np.uint8)
+    N, Kh = rows.shape
+    G = Kh // (GROUP // 2)
+    # [s, r, j, c, t] -> [s, j, c, r, t]
+    return np.ascontiguousarray(rows.reshape(N // 16, 16, G, 4, 16).transpose(0, 2, 3, 1, 4)
+                                .reshape(N // 16, G, 64, 16))
+
+
+def row_layout(slabs: np.ndarray) -> np.ndarray:
+    """Inverse of slab_layout: uint8 [N/16, K/128, 64, 16] -> [N, K/2]."""
+    slabs = np.asarray(slabs, dtype=np.uint8)
+    S, G = slabs.shape[:2]
+    # [s, j, c, r, t] -> [s, r, j, c, t]
+    return np.ascontiguousarray(slabs.reshape(S, G, 4, 16, 16).transpose(0, 3, 1, 2, 4)
+                                .reshape(S * 16, G * (GROUP // 2)))
+
+
 def build_csr(selected: np.ndarray, N: int, K: int, b: int):
     """CSR of selected blocks by output tile row: row_ptr[N/b+1], col_idx[n_sel] = kt."""
     sel = np.asarray(selected, dtype=np.int64)
@@ -244,9 +273,10 @@ def build_csr(selected: np.ndarray, N: int, K: int, b: int):
 def pack_weights(w: np.ndarray, b: int, selected: np.ndarray) -> dict:
     """Packed base + residual for the given (ascending) selected block ids.
 
-    qw uint8 [N, K/2], sw fp16 [N, G], row_ptr int32 [N/b+1], col_idx int32
-    [n_sel], qr uint8 [n_sel, b, b/2] (block row r = output nt*b+r, column
-    c = input kt*b+c), sr fp16 [n_sel, b].
+    qw uint8 [N/16, G, 64, 16] (slab_layout of the row-major packed codes),
+    sw fp16 [N, G], row_ptr int32 [N/b+1], col_idx int32 [n_sel], qr uint8
+    [n_sel, b, b/2] (block row r = output nt*b+r, column c = input kt*b+c),
+    sr fp16 [n_sel, b].
     """
     w16 = np.asarray(w, np.float16)
     N, K = w16.shape
@@ -263,14 +293,14 @@ def pack_weights(w: np.ndarray, b: int, selected: np.ndarray) -> dict:
         nt, kt = divmod(int(bid), KT)
         qr[i] = pack_nibbles(qrb[nt, :, kt, :])
         sr[i] = sr_all[nt, kt]
-    return dict(qw=pack_nibbles(qw), sw=sw, row_ptr=row_ptr, col_idx=col_idx,
+    return dict(qw=slab_layout(pack_nibbles(qw)), sw=sw, row_ptr=row_ptr, col_idx=col_idx,
                 qr=qr, sr=sr, block=b, N=N, K=K)
 
 
 def unpack_packed(packed: dict):
     """Codes back from a packed dict: (qw int8 [N,K], list of (nt, kt, qr int8 [b,b], sr fp16 [b]))."""
     b = packed["block"]
-    qw = unpack_nibbles(packed["qw"])
+    qw = unpack_nibbles(row_layout(packed["qw"]))
     blocks = []
     rp, ci = packed["row_ptr"], packed["col_idx"]
     for nt in range(len(rp) - 1):

@@ -62,7 +62,7 @@ def tile_rows_reference(qa_codes, sa, ref_packed: dict, tiles):
     outs = {}
     for nt in tiles:
         r0, r1 = int(ref_packed["row_ptr"][nt]), int(ref_packed["row_ptr"][nt + 1])
-        sub = dict(qw=ref_packed["qw"][nt * b:(nt + 1) * b], sw=ref_packed["sw"][nt * b:(nt + 1) * b],
+        sub = dict(qw=ref_packed["qw"][nt * b // 16:(nt + 1) * b // 16], sw=ref_packed["sw"][nt * b:(nt + 1) * b],
                    row_ptr=np.array([0, r1 - r0], np.int32), col_idx=ref_packed["col_idx"][r0:r1],
                    qr=ref_packed["qr"][r0:r1], sr=ref_packed["sr"][r0:r1], block=b, N=b, K=K)
         y, _, _ = oracle.fused_gemm(qa_codes, sa, sub)

@@ -78,13 +78,23 @@ def test_accumulators_against_brute_force_triple_loop():
     xc = rng.standard_normal((8, K)).astype(np.float16)
     ref = oracle.layer_reference(x, w, xc, b, 6)
     qa = [[int(v) for v in row] for row in ref["qa"]]
-    qw = oracle.unpack_nibbles(ref["packed"]["qw"]).tolist()
+    slabs = ref["packed"]["qw"]
+
+    def code(n, k):
+        # the slab layout by its definition: channel n is row n%16 of slab
+        # n//16; byte (k%128)//2 of its group segment sits in lane
+        # 16*(byte//16) + n%16 at position byte%16; even k in the low nibble
+        byte = (k % 128) // 2
+        v = int(slabs[n // 16, k // 128, 16 * (byte // 16) + n % 16, byte % 16])
+        v = (v >> 4) if k % 2 else (v & 15)
+        return v - 16 if v >= 8 else v
+
     for m in range(M):
         for n in range(N):
             for j in range(K // 128):
                 s = 0
                 for k in range(j * 128, (j + 1) * 128):
-                    s += qa[m][k] * qw[n][k]
+                    s += qa[m][k] * code(n, k)
                 assert ref["acc_base"][m, n, j] == s
     rp, ci = ref["packed"]["row_ptr"], ref["packed"]["col_idx"]
     i = 0
@@ -119,7 +129,7 @@ def test_pack_round_trip_and_csr():
     w = syn.make_weight(spec)
     sel = np.array([0, 3, 9, 10, 11, 40, 63])
     p = oracle.pack_weights(w, 64, sel)
-    assert p["qw"].shape == (512, 256) and p["qw"].dtype == np.uint8
+    assert p["qw"].shape == (32, 4, 64, 16) and p["qw"].dtype == np.uint8
     assert p["sw"].shape == (512, 4) and p["sw"].dtype == np.float16
     assert p["row_ptr"].tolist() == [0, 2, 5, 5, 5, 5, 6, 6, 7]
     assert p["col_idx"].tolist() == [0, 3, 1, 2, 3, 0, 7]
@@ -142,3 +152,17 @@ def test_tiny_reference_selects_ten_percent():
     assert spec.n_select == 6
     assert len(ref["selected"]) == 6 and ref["y"].shape == (16, 512)
     assert np.all(np.isfinite(ref["y"]))
+
+
+def test_slab_layout_by_definition_and_round_trip():
+    N, Kh = 48, 192                      # 3 slabs, 3 groups
+    rows = ((np.arange(N)[:, None] * 37 + np.arange(Kh)[None, :] * 11) % 251).astype(np.uint8)
+    slabs = oracle.slab_layout(rows)
+    assert slabs.shape == (3, 3, 64, 16)
+    for s_ in range(3):
+        for j in range(3):
+            for lane in range(64):
+                for t in range(16):
+                    n = 16 * s_ + lane % 16
+                    assert slabs[s_, j, lane, t] == rows[n, j * 64 + 16 * (lane // 16) + t]
+    assert np.array_equal(oracle.row_layout(slabs), rows)
