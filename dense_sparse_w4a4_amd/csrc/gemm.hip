@@ -57,12 +57,8 @@ namespace {
 // rows on different banks) and the A fragments are read from there.  The
 // fp16 loads are issued before the weight stream, so waiting for them never
 // waits on it.
-template <int BLK, int KS, bool DUMP, int QP>
+template <int BLK, int KS, bool DUMP, int QP, int U>
 __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
-  // groups per unit: four when the units carry only weight codes (the
-  // activation codes are in LDS), else three, which keeps every variant
-  // within 128 VGPRs (16 resident waves per CU, as the launcher assumes)
-  constexpr int U = QP > 0 ? 4 : 3;
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = (int)(a.K / kGroup);
   float* sa_t = reinterpret_cast<float*>(smem);  // [G][16]: sa/256 of the tile's tokens
@@ -318,30 +314,42 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   }
 }
 
-template <int BLK, int KS, bool DUMP, int QP>
+template <int BLK, int KS, bool DUMP, int QP, int U>
 hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t st) {
   const size_t lds = stream_lds_bytes(a.K, KS, QP > 0 ? (int)a.M : 0);
   if (lds > 64 * 1024) {
-    auto k = gemm_stream_kernel<BLK, KS, DUMP, QP>;
+    auto k = gemm_stream_kernel<BLK, KS, DUMP, QP, U>;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
   dim3 grid((unsigned)(a.N / 16), (unsigned)((a.M + 15) / 16));
-  hipLaunchKernelGGL((gemm_stream_kernel<BLK, KS, DUMP, QP>), grid, dim3(64 * KS), lds, st, a);
+  hipLaunchKernelGGL((gemm_stream_kernel<BLK, KS, DUMP, QP, U>), grid, dim3(64 * KS), lds, st, a);
   return hipGetLastError();
+}
+
+// Groups per streamed unit (two units in flight per wave): one when each
+// wave streams six or more groups, else two.  Shallow units keep fewer
+// weight bytes in flight per wave; measured on the Llama-3-8B decode shapes
+// with rotating weight copies, one-group units are fastest for the long
+// runs and two-group units for the short ones.
+template <int BLK, int KS, int QP>
+hipError_t launch_stream_u(const GemmArgs& a, hipStream_t st) {
+  if ((a.K / kGroup) / KS >= 6) return launch_stream_cfg<BLK, KS, false, QP, 1>(a, st);
+  return launch_stream_cfg<BLK, KS, false, QP, 2>(a, st);
 }
 
 template <int BLK, int KS>
 hipError_t launch_stream_ks(const GemmArgs& a, hipStream_t st) {
   if (a.x) {
     switch (stream_quant_passes(a.M, a.K, KS)) {
-      case 1: return launch_stream_cfg<BLK, KS, false, 1>(a, st);
-      case 2: return launch_stream_cfg<BLK, KS, false, 2>(a, st);
-      default: return launch_stream_cfg<BLK, KS, false, 4>(a, st);
+      case 1: return launch_stream_u<BLK, KS, 1>(a, st);
+      case 2: return launch_stream_u<BLK, KS, 2>(a, st);
+      default: return launch_stream_u<BLK, KS, 4>(a, st);
     }
   }
-  return a.acc_dump ? launch_stream_cfg<BLK, KS, true, 0>(a, st) : launch_stream_cfg<BLK, KS, false, 0>(a, st);
+  if (a.acc_dump) return launch_stream_cfg<BLK, KS, true, 0, 2>(a, st);
+  return launch_stream_u<BLK, KS, 0>(a, st);
 }
 
 template <int BLK>

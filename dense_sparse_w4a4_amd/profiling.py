@@ -68,6 +68,17 @@ def stats(outdir: str, prefix: str, title: str, cmd: str) -> str:
                 "|---|---:|---:|---:|---:|"]
         for (k, g, b), v in sorted(per.items()):
             out.append(f"| `{k}` | {g} | {b} | {len(v)} | {sum(v) / len(v):.2f} |")
+        # every template instance of a kernel together (the figure the
+        # benchmark's per-launch average compares with)
+        fam = defaultdict(list)
+        for (k, _, _), v in per.items():
+            for name in ("gemm_stream_kernel", "gemm_tile_kernel"):
+                if name in k:
+                    fam[name] += v
+        out += ["", "All launches per kernel (every template instance):", "",
+                "| kernel | calls | average (us) |", "|---|---:|---:|"]
+        for name, v in sorted(fam.items()):
+            out.append(f"| `{name}` | {len(v)} | {sum(v) / len(v):.2f} |")
     return "\n".join(out) + "\n"
 
 
