@@ -112,6 +112,10 @@ def test_fused_gemm_validation(L):
     assert _gemm(L, ldy=516) == ALIGN
     assert _gemm(L, qw=PMIS) == ALIGN
     assert _gemm(L, M=0, qa=None, y=None) == OK      # empty batch
+    # 32-bit kernel offsets: packed weights or activations of 4 GiB or more are refused
+    assert _gemm(L, N=65536, K=131072, ldy=65536, b=128) == SHAPE
+    assert "4 GiB" in ops.last_error()
+    assert _gemm(L, M=1 << 16, N=512, K=131072, b=128) == SHAPE
 
 
 def test_workspace_query(L):
