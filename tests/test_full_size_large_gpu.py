@@ -76,7 +76,7 @@ def _check(spec, Ms):
 
 @pytest.mark.parametrize("K,N", syn.QWEN3_32B_SHAPES)
 def test_full_size_qwen3_32b(K, N):
-    _check(syn.qwen3_32b(K, N), [1, 16])
+    _check(syn.qwen3_32b(K, N), [1, 16, 4096])
 
 
 def test_full_size_llama3_70b_ffn():
