@@ -28,12 +28,14 @@
 namespace mq {
 namespace {
 
-// Streaming kernel for small M (decode): 16 output channels x 16 tokens per
-// workgroup (grid.y walks 16-token tiles).  The KS waves of a workgroup
-// split the K groups into contiguous runs and reduce their partial sums
-// through LDS in wave order.  Activations are the MFMA A operand (rows =
-// tokens), weights the B operand (columns = channels): lane l owns channel
-// n0 + l%16 and tokens 4*(l/16) + i.
+// Streaming kernel for small M (decode): NS 16-channel slabs (16*NS output
+// channels, all inside one residual block row) x 16 tokens per workgroup
+// (grid.y walks 16-token tiles).  The KS waves of a workgroup split the K
+// groups into contiguous runs and reduce their partial sums through LDS in
+// wave order.  Activations are the MFMA A operand (rows = tokens), weights
+// the B operand (columns = channels): lane l owns channel l%16 of each slab
+// and tokens 4*(l/16) + i.  The slabs of a workgroup share one activation
+// fragment per group (and, with QP > 0, one in-prologue quantisation).
 //
 // The run of dense groups is streamed in units of U groups with two units
 // in flight: the loads of unit t+2 are issued before unit t+1 is computed.
@@ -41,11 +43,11 @@ namespace {
 // group and get scale 0), so the load counters are waited on exactly, and
 // the per-lane offsets are fixed: each unit only moves uniform bases.  The
 // tile's activation and weight scales are staged in LDS once.  The residual
-// blocks of the tile row follow as a second stream with the same item work
-// against the activation fragment of each block's group (the zipper); they
-// are dealt round-robin to the waves, so the waves finish together however
-// the selected blocks cluster in K, and the first one is loaded before the
-// dense stream starts.
+// blocks of the tile's block row follow as a second stream with the same
+// item work against the activation fragment of each block's group (the
+// zipper); they are dealt round-robin to the waves, so the waves finish
+// together however the selected blocks cluster in K, and the first two are
+// loaded before the dense stream starts.
 //
 // QP > 0 (M <= kStreamQuantRows, one token tile): the activations arrive as
 // fp16 and the workgroup quantises them itself before the streams start (the
@@ -53,20 +55,23 @@ namespace {
 // team of 16 lanes, 8 channels per lane; the scale is the same fp32 amax/7
 // as the standalone act-quant kernel and the codes come from the same
 // quotient (quant4_rcp), so codes, scales and y are identical to the
-// two-kernel path.  QP passes of the teams cover the tile's M x K/128 pairs.  Codes go to LDS rows of K/2 + 64 bytes (the pad puts the
-// rows on different banks) and the A fragments are read from there.  The
-// fp16 loads are issued before the weight stream, so waiting for them never
+// two-kernel path.  QP passes of the teams cover the tile's M x K/128
+// pairs.  Codes go to LDS rows of K/2 + 64 bytes (the pad puts the rows on
+// different banks) and the A fragments are read from there.  The fp16
+// loads are issued before the weight stream, so waiting for them never
 // waits on it.
-template <int BLK, int KS, bool DUMP, int QP, int U>
+template <int BLK, int KS, bool DUMP, int QP, int U, int NS>
 __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
+  static_assert(16 * NS <= BLK, "the slabs of a workgroup lie in one block row");
+  constexpr int CW = 16 * NS;  // channels per workgroup
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = (int)(a.K / kGroup);
   float* sa_t = reinterpret_cast<float*>(smem);  // [G][16]: sa/256 of the tile's tokens
-  float* sw_t = sa_t + G * 16;                     // [G][16]: weight scales of the tile's channels
-  float* spare = sa_t + 32 * G;                    // [2]: target of stores past the tables
-  unsigned char* qa_t = smem + stream_qa_offset(G);  // QP > 0: [M][qrow] activation codes
+  float* sw_t = sa_t + G * 16;                     // [G][CW]: weight scales of the tile's channels
+  float* spare = sw_t + G * CW;                    // [2]: target of stores past the tables
+  unsigned char* qa_t = smem + stream_qa_offset(G, NS);  // QP > 0: [M][qrow] activation codes
   const int qrow = (int)(a.K / 2) + 64;
-  float* red = reinterpret_cast<float*>(smem);   // [KS][16][17] after the streams
+  float* red = reinterpret_cast<float*>(smem);   // [KS][16][CW+1] after the streams
 
   // readfirstlane tells the compiler the wave index is uniform, so loop
   // bounds and bases stay scalar
@@ -74,25 +79,26 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   const int lane = threadIdx.x & 63;
   const int r16 = lane & 15;
   const int ch = lane >> 4;
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  const int64_t n0 = (int64_t)blockIdx.x * CW;
   const int64_t m0 = (int64_t)blockIdx.y * 16;
   const int64_t Kh = a.K / 2;
   const int gb = wave * G / KS;
   const int ng = (wave + 1) * G / KS - gb;
 
   // per-lane byte offsets (32-bit: the host keeps N*K/2 and M*K/2 below 2^32)
-  // weight codes in the slab layout: the tile is one 16-channel slab and
-  // each group of it is 1 KB, lane l's 16 bytes at l*16, so every weight
-  // load of a wave reads 1 KB contiguous
+  // weight codes in the slab layout: each group of a slab is 1 KB, lane l's
+  // 16 bytes at l*16, so every weight load of a wave reads 1 KB contiguous;
+  // the workgroup's slabs are 16*K/2 bytes apart
   const uint32_t offW = (uint32_t)(n0 * Kh + lane * 16);
+  const uint32_t slabW = (uint32_t)(16 * Kh);
   const int64_t mr = m0 + r16;  // token rows past M read row M-1 (computed, never stored)
   const uint32_t offX = (uint32_t)((mr < a.M ? mr : a.M - 1) * Kh + ch * 16);
   const int offXl = (int)((mr < a.M ? mr : a.M - 1) - m0) * qrow + ch * 16;  // QP > 0: in qa_t
   auto lds_x = [&](int j) { return *reinterpret_cast<const uint4*>(qa_t + offXl + j * 64); };
 
   struct Unit {
-    uint4 W[U];  // B-operand fragments (weight codes)
-    uint4 X[U];  // A-operand fragments (activation codes)
+    uint4 W[U][NS];  // B-operand fragments (weight codes), per group and slab
+    uint4 X[U];      // A-operand fragments (activation codes), per group
   };
 
   // dense unit t: groups gb + t*U + u, clamped to the run
@@ -100,32 +106,36 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int j = gb + min(t * U + u, ng - 1);
-      D.W[u] = ld16(a.qw + (int64_t)j * 1024 + offW);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) D.W[u][s] = ld16(a.qw + (int64_t)j * 1024 + offW + s * slabW);
       if constexpr (QP == 0) D.X[u] = ld16(a.qa + (int64_t)j * 64 + offX);
     }
   };
 
-  float y[4] = {0.f, 0.f, 0.f, 0.f};
+  float y[NS][4];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) y[s][0] = y[s][1] = y[s][2] = y[s][3] = 0.f;
   const v4i zero = {0, 0, 0, 0};
 
-  // one item: two MFMAs, then y += (sa/256 * s) * acc for the lane's tokens
-  // (s = the item's weight or residual row scale, 0 for padding)
-  auto item = [&](const uint4& W, const uint4& X, float sc, uint32_t rm, int j, bool valid,
+  // one item of slab s: two MFMAs, then y += (sa/256 * sc) * acc for the
+  // lane's tokens (sc = the item's weight or residual row scale, 0 for
+  // padding)
+  auto item = [&](int s, const uint4& W, const uint4& X, float sc, uint32_t rm, int j, bool valid,
                   int64_t dump_at, bool dump_res) {
     v4i acc = mfma(widen8(X.x, X.y), widen8(W.x & rm, W.y & rm), zero);
     acc = mfma(widen8(X.z, X.w), widen8(W.z & rm, W.w & rm), acc);
     const float4 s4 = *reinterpret_cast<const float4*>(sa_t + j * 16 + 4 * ch);
-    y[0] = fmaf(s4.x * sc, (float)acc[0], y[0]);
-    y[1] = fmaf(s4.y * sc, (float)acc[1], y[1]);
-    y[2] = fmaf(s4.z * sc, (float)acc[2], y[2]);
-    y[3] = fmaf(s4.w * sc, (float)acc[3], y[3]);
+    y[s][0] = fmaf(s4.x * sc, (float)acc[0], y[s][0]);
+    y[s][1] = fmaf(s4.y * sc, (float)acc[1], y[s][1]);
+    y[s][2] = fmaf(s4.z * sc, (float)acc[2], y[s][2]);
+    y[s][3] = fmaf(s4.w * sc, (float)acc[3], y[s][3]);
     if (DUMP && valid) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t m = m0 + 4 * ch + i;
         if (m < a.M) {
           if (!dump_res)
-            a.acc_dump[(m * a.N + n0 + r16) * G + j] = acc[i] >> 8;
+            a.acc_dump[(m * a.N + n0 + 16 * s + r16) * G + j] = acc[i] >> 8;
           else
             a.acc_dump[dump_at + m * BLK] = acc[i] >> 8;
         }
@@ -137,14 +147,17 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
     for (int u = 0; u < U; ++u) {
       const bool valid = t * U + u < ng;
       const int j = gb + min(t * U + u, ng - 1);
-      item(D.W[u], QP > 0 ? lds_x(j) : D.X[u], valid ? sw_t[j * 16 + r16] : 0.f, 0xFFFFFFFFu, j,
-           valid, 0, false);
+      const uint4 X = QP > 0 ? lds_x(j) : D.X[u];
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        item(s, D.W[u][s], X, valid ? sw_t[j * CW + 16 * s + r16] : 0.f, 0xFFFFFFFFu, j, valid, 0,
+             false);
     }
   };
 
   // ---- prologue: the tile's scale loads first, then two dense units and
-  // the CSR window in flight; the scales go to LDS (transposed to [G][16])
-  // as soon as they arrive, without waiting for the units ----
+  // the CSR window in flight; the scales go to LDS (transposed to [G][16]
+  // and [G][CW]) as soon as they arrive, without waiting for the units ----
   const int nunits = (ng + U - 1) / U;
   // QP > 0: the fp16 activations of the tile's (token, group) pairs, one
   // 16-byte load per pass and lane, all issued first (the launcher picks QP
@@ -160,21 +173,27 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
       xv[it] = *reinterpret_cast<const uint4*>(a.x + (m0 + row) * a.ldx + j * kGroup + tl * 8);
     }
   }
-  constexpr int SMAX = 4;  // staged scale pairs issued ahead, per thread
-  const int nst = 16 * G;
+  constexpr int SMAX = 4;       // staged activation scales issued ahead, per thread
+  constexpr int WMAX = 4 * NS;  // staged weight scales issued ahead, per thread
+  const int nsa = 16 * G, nsw = CW * G;
   const uint8_t* sa_b = reinterpret_cast<const uint8_t*>(a.sa);
   const uint8_t* sw_b = reinterpret_cast<const uint8_t*>(a.sw) + n0 * G * 2;
   float pa[SMAX];
-  uint16_t pw[SMAX];
+  uint16_t pw[WMAX];
 #pragma unroll
   for (int k = 0; k < SMAX; ++k) {
-    const int i = min((int)threadIdx.x + k * 64 * KS, nst - 1);
-    const int mm = i / G, j = i - mm * G;
-    const int64_t m = m0 + mm;
-    if constexpr (QP == 0)
+    if constexpr (QP == 0) {
+      const int i = min((int)threadIdx.x + k * 64 * KS, nsa - 1);
+      const int mm = i / G, j = i - mm * G;
+      const int64_t m = m0 + mm;
       pa[k] = *reinterpret_cast<const float*>(sa_b + (uint32_t)(((m < a.M ? m : a.M - 1) * G + j) * 4));
-    else
+    } else {
       pa[k] = 0.f;
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < WMAX; ++k) {
+    const int i = min((int)threadIdx.x + k * 64 * KS, nsw - 1);
     pw[k] = *reinterpret_cast<const uint16_t*>(sw_b + (uint32_t)(i * 2));
   }
   // (every wave has at least one group: the launcher keeps KS <= G; the
@@ -183,9 +202,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   fetch_dense(U0, 0);
   fetch_dense(U1, 1);
 
-  // Residual CSR row of this tile (block row nt, block rows rrow .. rrow+15).
-  // The CSR arrays are read through the scalar cache (uniform addresses, a
-  // read-only view), so their waits never involve the vector loads in flight.
+  // Residual CSR row of this tile (block row nt; the tile's channels are
+  // block rows rrow .. rrow + CW - 1).  The CSR arrays are read through the
+  // scalar cache (uniform addresses, a read-only view), so their waits never
+  // involve the vector loads in flight.
   typedef const __attribute__((address_space(4))) int32_t* cint_p;
   const cint_p rpc = (cint_p)a.row_ptr;
   const cint_p cic = (cint_p)a.col_idx;
@@ -197,7 +217,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
     rp1 = min(max(rpc[nt + 1], rp0), a.n_select);
   }
   // this wave's residual entries are rp0 + wave + KS*k (see below); the
-  // first one's block column is fetched now
+  // first two block columns are fetched now
   const int nres = rp1 > rp0 ? (rp1 - rp0 - wave + KS - 1) / KS : 0;
   auto res_kt = [&](int k) { return cic[rp0 + wave + KS * k]; };
   const int kt_first = nres > 0 ? res_kt(0) : 0;
@@ -211,46 +231,61 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   // weight codes and scales), so the prologue's load counters are waited on
   // exactly; later entries are loaded only when they exist, so no load is
   // left in flight at the end ----
-  auto res_ptrs = [&](int k, int kt, uint4& W, uint4& X, uint32_t& S, uint32_t& rm, int& j) {
+  struct Res {
+    uint4 W[NS];
+    uint4 X;
+    uint32_t S[NS];
+    uint32_t rm;
+    int j;
+  };
+  auto res_ptrs = [&](int k, int kt, Res& R) {
     const bool has = k < nres;
     const int e = has ? rp0 + wave + KS * k : 0;
-    j = kt * BLK / kGroup;
-    const int lo = kt * BLK - j * kGroup;
+    R.j = kt * BLK / kGroup;
+    const int lo = kt * BLK - R.j * kGroup;
     const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK);
-    rm = act ? 0xFFFFFFFFu : 0u;
-    W = ld16(has ? a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + r16) * (BLK / 2) + (act ? 16 * ch - lo / 2 : 0)
-                 : a.qw + offW);
-    if constexpr (QP == 0) X = ld16(a.qa + (int64_t)j * 64 + offX);
-    S = *(has ? a.sr + (int64_t)e * BLK + rrow + r16 : a.sw);
+    R.rm = act ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      R.W[s] = ld16(has ? a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + 16 * s + r16) * (BLK / 2) +
+                              (act ? 16 * ch - lo / 2 : 0)
+                        : a.qw + offW);
+      R.S[s] = *(has ? a.sr + (int64_t)e * BLK + rrow + 16 * s + r16 : a.sw);
+    }
+    if constexpr (QP == 0) R.X = ld16(a.qa + (int64_t)R.j * 64 + offX);
   };
   // the first two entries are loaded now, before the scale staging, so they
   // arrive during the dense stream
-  uint4 W0, X0, W1, X1;
-  uint32_t S0 = 0, S1 = 0, rm0 = 0, rm1 = 0;
-  int j0 = 0, j1 = 0;
-  res_ptrs(0, kt_first, W0, X0, S0, rm0, j0);
-  res_ptrs(1, kt_second, W1, X1, S1, rm1, j1);
+  Res R0, R1;
+  res_ptrs(0, kt_first, R0);
+  res_ptrs(1, kt_second, R1);
 
   // (stores past the tables go to the spare slots, so no store is branched
   // and the waits stay exact; with QP > 0 the activation scales of the
   // tile's tokens come from the quantisation below and only the padding
   // rows are written here)
-  auto stage = [&](int i, float v, uint16_t w) {
+  auto stage_a = [&](int i, float v) {
     const int mm = i / G, j = i - mm * G;
-    const bool in = i < nst;
     const bool pad = m0 + mm >= a.M;
-    float* const da = in && (QP == 0 || pad) ? sa_t + j * 16 + mm : spare;
-    float* const dw = in ? sw_t + j * 16 + mm : spare + 1;
+    float* const da = i < nsa && (QP == 0 || pad) ? sa_t + j * 16 + mm : spare;
     *da = pad ? 0.f : v * kInv256;
+  };
+  auto stage_w = [&](int i, uint16_t w) {
+    const int r = i / G, j = i - r * G;
+    float* const dw = i < nsw ? sw_t + j * CW + r : spare + 1;
     *dw = h2f(w);
   };
 #pragma unroll
-  for (int k = 0; k < SMAX; ++k) stage((int)threadIdx.x + k * 64 * KS, pa[k], pw[k]);
-  for (int i = (int)threadIdx.x + SMAX * 64 * KS; i < nst; i += 64 * KS) {  // long K only
+  for (int k = 0; k < SMAX; ++k) stage_a((int)threadIdx.x + k * 64 * KS, pa[k]);
+#pragma unroll
+  for (int k = 0; k < WMAX; ++k) stage_w((int)threadIdx.x + k * 64 * KS, pw[k]);
+  for (int i = (int)threadIdx.x + SMAX * 64 * KS; i < nsa; i += 64 * KS) {  // long K only
     const int mm = i / G, j = i - mm * G;
     const int64_t m = m0 + mm;
-    stage(i, QP == 0 ? a.sa[(m < a.M ? m : a.M - 1) * G + j] : 0.f, a.sw[(n0 + mm) * G + j]);
+    stage_a(i, QP == 0 ? a.sa[(m < a.M ? m : a.M - 1) * G + j] : 0.f);
   }
+  for (int i = (int)threadIdx.x + WMAX * 64 * KS; i < nsw; i += 64 * KS)  // long K only
+    stage_w(i, a.sw[(n0 + i / G) * G + i % G]);
   if constexpr (QP > 0) {
     // quantise the tile: pass it covers pairs team + it * (4 KS), clamped
     // to the last pair, so every pass is branch-free and teams past the end
@@ -265,21 +300,24 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
       amax = row16_max(amax);
-      const float s = amax / 7.0f;
-      const float r = s == 0.0f ? 0.0f : 1.0f / s;
+      const float sc = amax / 7.0f;
+      const float r = sc == 0.0f ? 0.0f : 1.0f / sc;
       int q[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = quant4_rcp(f[i], s, r);
+      for (int i = 0; i < 8; ++i) q[i] = quant4_rcp(f[i], sc, r);
       *reinterpret_cast<uint32_t*>(qa_t + row * qrow + j * 64 + tl * 4) = pack8(q);
-      if (tl == 0) sa_t[j * 16 + row] = s * kInv256;
+      if (tl == 0) sa_t[j * 16 + row] = sc * kInv256;
     }
   }
   __syncthreads();
 
-  auto res_item = [&](int k, const uint4& W, const uint4& X, uint32_t S, uint32_t rm, int j) {
+  auto res_item = [&](int k, const Res& R) {
     const int64_t e = rp0 + wave + KS * k;
-    item(W, QP > 0 ? lds_x(j) : X, h2f((uint16_t)S), rm, j, true,
-         a.M * a.N * G + e * a.M * BLK + rrow + r16, true);
+    const uint4 X = QP > 0 ? lds_x(R.j) : R.X;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      item(s, R.W[s], X, h2f((uint16_t)R.S[s]), R.rm, R.j, true,
+           a.M * a.N * G + e * a.M * BLK + rrow + 16 * s + r16, true);
   };
   // ---- dense stream (ping-pong buffers, never copied while in flight) ----
   for (int t = 0; t < nunits; t += 2) {
@@ -293,91 +331,99 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   // ---- residual stream: the same item work against the activation
   // fragment of each block's group, two entries in flight ----
   for (int k = 0; k < nres; k += 2) {
-    res_item(k, W0, X0, S0, rm0, j0);
-    if (k + 2 < nres) res_ptrs(k + 2, res_kt(k + 2), W0, X0, S0, rm0, j0);
+    res_item(k, R0);
+    if (k + 2 < nres) res_ptrs(k + 2, res_kt(k + 2), R0);
     if (k + 1 >= nres) break;
-    res_item(k + 1, W1, X1, S1, rm1, j1);
-    if (k + 3 < nres) res_ptrs(k + 3, res_kt(k + 3), W1, X1, S1, rm1, j1);
+    res_item(k + 1, R1);
+    if (k + 3 < nres) res_ptrs(k + 3, res_kt(k + 3), R1);
   }
 
   __syncthreads();  // scales no longer needed: reuse LDS for the reduction
 #pragma unroll
-  for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * ch + i) * 17 + r16] = y[i];
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < 256; idx += 64 * KS) {
-    const int mm = idx >> 4, nl = idx & 15;
-    float s = 0.f;
+  for (int s = 0; s < NS; ++s)
 #pragma unroll
-    for (int w = 0; w < KS; ++w) s += red[(w * 16 + mm) * 17 + nl];
+    for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * ch + i) * (CW + 1) + 16 * s + r16] = y[s][i];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 16 * CW; idx += 64 * KS) {
+    const int mm = idx / CW, nl = idx - mm * CW;
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < KS; ++w) sum += red[(w * 16 + mm) * (CW + 1) + nl];
     const int64_t m = m0 + mm;
-    if (m < a.M) a.y[m * a.ldy + n0 + nl] = f2h_bits(s);
+    if (m < a.M) a.y[m * a.ldy + n0 + nl] = f2h_bits(sum);
   }
 }
 
-template <int BLK, int KS, bool DUMP, int QP, int U>
+template <int BLK, int KS, bool DUMP, int QP, int U, int NS>
 hipError_t launch_stream_cfg(const GemmArgs& a, hipStream_t st) {
-  const size_t lds = stream_lds_bytes(a.K, KS, QP > 0 ? (int)a.M : 0);
+  const size_t lds = stream_lds_bytes(a.K, KS, QP > 0 ? (int)a.M : 0, NS);
   if (lds > 64 * 1024) {
-    auto k = gemm_stream_kernel<BLK, KS, DUMP, QP, U>;
+    auto k = gemm_stream_kernel<BLK, KS, DUMP, QP, U, NS>;
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  dim3 grid((unsigned)(a.N / 16), (unsigned)((a.M + 15) / 16));
-  hipLaunchKernelGGL((gemm_stream_kernel<BLK, KS, DUMP, QP, U>), grid, dim3(64 * KS), lds, st, a);
+  dim3 grid((unsigned)(a.N / (16 * NS)), (unsigned)((a.M + 15) / 16));
+  hipLaunchKernelGGL((gemm_stream_kernel<BLK, KS, DUMP, QP, U, NS>), grid, dim3(64 * KS), lds, st, a);
   return hipGetLastError();
 }
 
-// Groups per streamed unit (two units in flight per wave): one when each
-// wave streams six or more groups, else two.  Shallow units keep fewer
-// weight bytes in flight per wave; measured on the Llama-3-8B decode shapes
-// with rotating weight copies, one-group units are fastest for the long
-// runs and two-group units for the short ones.
-template <int BLK, int KS, int QP>
-hipError_t launch_stream_u(const GemmArgs& a, hipStream_t st) {
-  if ((a.K / kGroup) / KS >= 6) return launch_stream_cfg<BLK, KS, false, QP, 1>(a, st);
-  return launch_stream_cfg<BLK, KS, false, QP, 2>(a, st);
+template <int BLK, int KS, int NS, int QP>
+hipError_t launch_stream_u(const GemmArgs& a, const StreamPlan& p, hipStream_t st) {
+  if constexpr (NS == 1) {
+    if (p.u == 2) return launch_stream_cfg<BLK, KS, false, QP, 2, NS>(a, st);
+  }
+  return launch_stream_cfg<BLK, KS, false, QP, 1, NS>(a, st);
 }
 
-template <int BLK, int KS>
-hipError_t launch_stream_ks(const GemmArgs& a, hipStream_t st) {
+template <int BLK, int KS, int NS>
+hipError_t launch_stream_ks(const GemmArgs& a, const StreamPlan& p, hipStream_t st) {
   if (a.x) {
-    switch (stream_quant_passes(a.M, a.K, KS)) {
-      case 1: return launch_stream_u<BLK, KS, 1>(a, st);
-      case 2: return launch_stream_u<BLK, KS, 2>(a, st);
-      default: return launch_stream_u<BLK, KS, 4>(a, st);
+    switch (p.qp) {
+      case 1: return launch_stream_u<BLK, KS, NS, 1>(a, p, st);
+      case 2: return launch_stream_u<BLK, KS, NS, 2>(a, p, st);
+      default: return launch_stream_u<BLK, KS, NS, 4>(a, p, st);
     }
   }
-  if (a.acc_dump) return launch_stream_cfg<BLK, KS, true, 0, 2>(a, st);
-  return launch_stream_u<BLK, KS, 0>(a, st);
+  if constexpr (NS == 1) {
+    if (a.acc_dump) return launch_stream_cfg<BLK, KS, true, 0, 2, 1>(a, st);
+  }
+  return launch_stream_u<BLK, KS, NS, 0>(a, p, st);
+}
+
+template <int BLK, int NS>
+hipError_t launch_stream_ns(const GemmArgs& a, const StreamPlan& p, hipStream_t st) {
+  switch (p.ks) {
+    case 16: return launch_stream_ks<BLK, 16, NS>(a, p, st);
+    case 8: return launch_stream_ks<BLK, 8, NS>(a, p, st);
+    case 4: return launch_stream_ks<BLK, 4, NS>(a, p, st);
+    case 2: return launch_stream_ks<BLK, 2, NS>(a, p, st);
+    default: return launch_stream_ks<BLK, 1, NS>(a, p, st);
+  }
 }
 
 template <int BLK>
 hipError_t launch_blk(const GemmArgs& a, hipStream_t st) {
-  switch (stream_waves(a.M, a.N, a.K)) {
-    case 16: return launch_stream_ks<BLK, 16>(a, st);
-    case 8: return launch_stream_ks<BLK, 8>(a, st);
-    case 4: return launch_stream_ks<BLK, 4>(a, st);
-    case 2: return launch_stream_ks<BLK, 2>(a, st);
-    default: return launch_stream_ks<BLK, 1>(a, st);
-  }
+  const StreamPlan p = stream_plan(a.M, a.N, a.K, BLK, a.x != nullptr, a.acc_dump != nullptr);
+  if (p.ns == 2) return launch_stream_ns<BLK, 2>(a, p, st);
+  return launch_stream_ns<BLK, 1>(a, p, st);
 }
 
 }  // namespace
 
-size_t stream_lds_bytes(int64_t K, int ks, int rows) {
+size_t stream_lds_bytes(int64_t K, int ks, int rows, int ns) {
   const int64_t G = K / kGroup;
-  const size_t stage = (size_t)stream_qa_offset((int)G) + (size_t)rows * (size_t)(K / 2 + 64);
-  const size_t reduce = (size_t)ks * 16 * 17 * 4;
+  const size_t stage = (size_t)stream_qa_offset((int)G, ns) + (size_t)rows * (size_t)(K / 2 + 64);
+  const size_t reduce = (size_t)ks * 16 * (16 * ns + 1) * 4;
   return stage > reduce ? stage : reduce;
 }
 
 // Waves per tile: the most (up to 16) that keep the grid within one
 // resident round (<= 4096 waves, 16 per CU) and give every wave at least
 // one unit of 4 groups.
-int stream_waves(int64_t M, int64_t N, int64_t K) {
+int stream_waves(int64_t M, int64_t N, int64_t K, int ns) {
   const int64_t G = K / kGroup;
-  const int64_t tiles = (N / 16) * ((M + 15) / 16);
+  const int64_t tiles = (N / (16 * ns)) * ((M + 15) / 16);
   if (tiles * 16 <= 4096 && G >= 64) return 16;
   if (tiles * 8 <= 4096 && G >= 32) return 8;
   if (tiles * 4 <= 4096 && G >= 16) return 4;
@@ -398,10 +444,44 @@ int stream_quant_passes(int64_t M, int64_t K, int ks) {
   return 0;
 }
 
+// Slabs per workgroup: two when that keeps the grid's wave count and every
+// wave still streams eight or more groups, else one.  Measured with
+// rotating weights: two slabs (one activation fragment for both) win on the
+// Qwen3-32B decode shapes (long per-wave runs; up to 1.3x at M = 16) and
+// lose where they halve the waves or shorten the runs (Llama-3-8B shapes).
+// Four would need more than the 128 VGPRs that keep 16 waves resident per
+// CU.
+static int stream_slabs(int64_t M, int64_t N, int64_t K, int block) {
+  if (block < 32 || N % 32 != 0) return 1;
+  const int64_t mt = (M + 15) / 16;
+  const int ks1 = stream_waves(M, N, K, 1), ks2 = stream_waves(M, N, K, 2);
+  const bool same_waves = (N / 32) * mt * ks2 >= (N / 16) * mt * ks1;
+  return same_waves && (K / kGroup) / ks2 >= 8 ? 2 : 1;
+}
+
+StreamPlan stream_plan(int64_t M, int64_t N, int64_t K, int block, bool quantise, bool dump) {
+  StreamPlan p;
+  p.ns = dump ? 1 : stream_slabs(M, N, K, block);
+  p.ks = stream_waves(M, N, K, p.ns);
+  // groups per streamed unit (two units in flight per wave): one when each
+  // wave streams six or more groups, else two (slab groups: always one).
+  // Shallow units keep fewer weight bytes in flight per wave; measured on
+  // the Llama-3-8B decode shapes with rotating weight copies, one-group units
+  // are fastest for the long runs and two-group units for the short ones.
+  p.u = (p.ns == 1 && (K / kGroup) / p.ks < 6) ? 2 : 1;
+  p.qp = quantise ? stream_quant_passes(M, K, p.ks) : 0;
+  return p;
+}
+
 bool stream_quant_fits(int64_t M, int64_t N, int64_t K) {
   if (M < 1 || M > kStreamQuantRows) return false;
-  const int ks = stream_waves(M, N, K);
-  return stream_quant_passes(M, K, ks) > 0 && stream_lds_bytes(K, ks, (int)M) <= 64 * 1024;
+  // whatever the residual block edge, the plan must quantise in the prologue
+  for (int block : {32, 64, 128}) {
+    if (N % block != 0) continue;
+    const StreamPlan p = stream_plan(M, N, K, block, true, false);
+    if (p.qp == 0 || stream_lds_bytes(K, p.ks, (int)M, p.ns) > 64 * 1024) return false;
+  }
+  return true;
 }
 
 hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st) {

@@ -128,12 +128,19 @@ struct GemmArgs {
 // 4 passes of the workgroup's 16-lane teams.
 constexpr int kStreamQuantRows = 4;
 // LDS byte offset of the streaming kernel's activation codes: after the
-// [G][16] activation and weight scale tables and two spare slots.
-__host__ __device__ constexpr int stream_qa_offset(int G) { return 128 * G + 16; }
-int stream_waves(int64_t M, int64_t N, int64_t K);
+// [G][16] activation and [G][16*ns] weight scale tables and the spare slots.
+__host__ __device__ constexpr int stream_qa_offset(int G, int ns) { return (64 + 64 * ns) * G + 16; }
+// Launch shape of the streaming kernel: 16-channel slabs per workgroup,
+// waves per workgroup, groups per streamed unit, quantisation passes (0:
+// the activations arrive as codes).
+struct StreamPlan {
+  int ns, ks, u, qp;
+};
+StreamPlan stream_plan(int64_t M, int64_t N, int64_t K, int block, bool quantise, bool dump);
+int stream_waves(int64_t M, int64_t N, int64_t K, int ns);
 int stream_quant_passes(int64_t M, int64_t K, int ks);
 bool stream_quant_fits(int64_t M, int64_t N, int64_t K);
-size_t stream_lds_bytes(int64_t K, int ks, int rows);
+size_t stream_lds_bytes(int64_t K, int ks, int rows, int ns);
 
 hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st);
 hipError_t launch_residual_merge(const GemmArgs& a, hipStream_t st);
