@@ -45,10 +45,12 @@ __global__ __launch_bounds__(64 * (BLK / 16)) void residual_merge_kernel(GemmArg
 #pragma unroll
     for (int c = 0; c < C; ++c) {
       const int e = min(eb + c, e1 - 1);
-      const int kt = a.col_idx[e];
+      const int kt_in = a.col_idx[e];
+      const bool okt = kt_in >= 0 && kt_in < (int)(a.K / BLK);  // else the entry adds nothing
+      const int kt = okt ? kt_in : 0;
       const int j = kt * BLK / kGroup;
       const int lo = kt * BLK - j * kGroup;
-      const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK) && (eb + c < e1);
+      const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK) && (eb + c < e1) && okt;
       rm[c] = act ? 0xFFFFFFFFu : 0u;
       jj[c] = j;
       W[c] = ld16(a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + r16) * (BLK / 2) + (act ? 16 * ch - lo / 2 : 0));

@@ -238,12 +238,16 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
     uint32_t rm;
     int j;
   };
-  auto res_ptrs = [&](int k, int kt, Res& R) {
+  // (an entry whose block column is outside [0, K/b) contributes nothing:
+  // its codes are masked and its group index clipped)
+  auto res_ptrs = [&](int k, int kt_in, Res& R) {
+    const bool okt = kt_in >= 0 && kt_in < (int)(a.K / BLK);
+    const int kt = okt ? kt_in : 0;
     const bool has = k < nres;
     const int e = has ? rp0 + wave + KS * k : 0;
     R.j = kt * BLK / kGroup;
     const int lo = kt * BLK - R.j * kGroup;
-    const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK);
+    const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK) && okt;
     R.rm = act ? 0xFFFFFFFFu : 0u;
 #pragma unroll
     for (int s = 0; s < NS; ++s) {

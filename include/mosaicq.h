@@ -172,7 +172,11 @@ mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes
  *              mq_pack_weights; n_select == 0 gives the dense-only layer
  *              (row_ptr, col_idx, qr, sr may then be NULL).  A CSR that
  *              points outside [0, n_select) or past K is clipped, never
- *              read out of bounds (check it with mq_validate_csr).
+ *              read out of bounds: row ranges are clipped to [0, n_select]
+ *              and made non-decreasing, and an entry whose block column is
+ *              outside [0, K/block) contributes nothing.  Other invalid
+ *              CSRs (unsorted or repeated columns in a row) give
+ *              unspecified but finite y.  Check a CSR with mq_validate_csr.
  *   y        : fp16 [M][ldy], ldy >= N, ldy % 8 == 0 (output)
  *   workspace: device buffer of workspace_bytes (16-byte aligned) or NULL.
  *              With at least mq_fused_gemm_workspace's bytes the split-K

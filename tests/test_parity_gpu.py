@@ -330,3 +330,74 @@ def test_smooth_bit_exact():
     assert np.array_equal(host(x2).view(np.uint16), oracle.smooth_acts(x, rs).view(np.uint16))
     assert np.array_equal(host(ax), np.abs(xc.astype(np.float32)).max(0))
     assert np.array_equal(host(aw), np.abs(w.astype(np.float32)).max(0))
+
+
+def _sanitized(ref, row_ptr, col_idx):
+    """The residual the kernels use for an arbitrary CSR: per block row, the
+    entries [clip(rp[nt]), clip(rp[nt+1])) with rp clipped to [0, n_select]
+    and non-decreasing, minus entries whose block column is out of range."""
+    ns = len(ref["qr"])
+    KT = ref["K"] // ref["block"]
+    keep, rows = [], [0]
+    for nt in range(len(row_ptr) - 1):
+        e0 = min(max(int(row_ptr[nt]), 0), ns)
+        e1 = min(max(int(row_ptr[nt + 1]), e0), ns)
+        kept = [e for e in range(e0, e1) if 0 <= int(col_idx[e]) < KT]
+        keep += kept
+        rows.append(rows[-1] + len(kept))
+    keep = np.array(keep, dtype=np.int64)
+    return dict(ref, row_ptr=np.array(rows, np.int32), col_idx=col_idx[keep].astype(np.int32),
+                qr=ref["qr"][keep], sr=ref["sr"][keep])
+
+
+@pytest.mark.parametrize("M,merge", [(5, False), (70, False), (5, True), (70, True)])
+def test_corrupt_csr_is_clipped_not_read_out_of_bounds(M, merge):
+    # a CSR the validator rejects: row pointers past n_select or negative,
+    # block columns outside [0, K/b), and (merge) a negative then an
+    # oversized pointer that make one block row span every entry.  The
+    # kernels clip the row ranges and skip out-of-range columns, so every
+    # access stays in bounds.  The streaming kernel (M = 5) adds every entry
+    # of a row, which is the sanitised reference below; the tile kernel
+    # (M = 70) keeps one entry per (row, column), so where clipping merges
+    # rows that hold the same column its output is only required to be
+    # finite.
+    N, K, b = 256, 1024, 64
+    spec = syn.LayerSpec("c", K=K, N=N, T=32, block=b, rho=0.25)
+    w, xc = _layer(spec, seed=11)
+    rsel, _, _ = oracle.select_blocks(w, xc, b, spec.n_select)
+    ref = oracle.pack_weights(w, b, rsel)
+    ns = len(rsel)
+    rp = ref["row_ptr"].copy()
+    ci = ref["col_idx"].copy()
+    rp[0] = -3
+    rp[-1] = ns + 7
+    ci[0] = -5
+    ci[min(3, ns - 1)] = K // b + 3
+    if merge:
+        rp[1] = -3
+        rp[2] = ns + 7
+    layer = ops.PackedLayer(N, K, b, dev(ref["qw"]), dev(ref["sw"]), dev(rp), dev(ci),
+                            dev(ref["qr"]), dev(ref["sr"]))
+    with pytest.raises(ops.MosaicQError):
+        ops.validate_csr(layer)
+    x = syn.make_acts(spec, M, seed=3)
+    rqa, rsa = oracle.quantize_act(x)
+    qa, sa = dev(oracle.pack_nibbles(rqa)), dev(rsa)
+    print(f"corrupt CSR M={M} merge={merge}", flush=True)
+    y = ops.fused_gemm(qa, sa, layer)
+    # the unfused ablation on the same CSR: dense-only GEMM, then the merge
+    dense = ops.PackedLayer(N, K, b, layer.qw, layer.sw, torch.zeros_like(layer.row_ptr),
+                            layer.col_idx[:0], layer.qr[:0], layer.sr[:0])
+    yu = ops.fused_gemm(qa, sa, dense)
+    ops.residual_merge(qa, sa, layer, yu)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(host(y).astype(np.float64)))
+    assert np.all(np.isfinite(host(yu).astype(np.float64)))
+    y_ref, _, _ = oracle.fused_gemm(rqa, rsa, _sanitized(ref, rp, ci))
+    yd_ref, _, _ = oracle.fused_gemm(rqa, rsa, dict(ref, row_ptr=np.zeros_like(rp), col_idx=ci[:0],
+                                                    qr=ref["qr"][:0], sr=ref["sr"][:0]))
+    bound = 1e-3 * np.maximum(np.abs(y_ref), np.sqrt(np.mean(y_ref ** 2))) + 2.0 ** -12 * np.abs(yd_ref)
+    # the standalone residual kernel adds every entry, like the streaming kernel
+    assert np.all(np.abs(host(yu).astype(np.float64) - y_ref) <= bound)
+    if M <= 32 or not merge:
+        assert_y_close(y, y_ref)
