@@ -25,14 +25,13 @@
 // 32-wide block with one MFMA on half of the lanes, a 128-wide block with
 // both, and each block keeps its own accumulator and row scale.
 //
-// Epilogue: per 16x16 tile and group, y += (sa[m]*sw[n]) * acc[m][n].  The
-// 256 scale products of a tile form an outer product, so the matrix core
-// computes them with one bf16 MFMA: sa (fp32) is split exactly into three
-// bf16 parts and sw (fp16) into two, the six partial products go to six k
-// slots, and the fp32 accumulation returns sa*sw to within a few fp32 ulps
-// over the whole fp32 range.  The vector unit keeps one int->float
-// conversion and one FMA per element and group.  The factor 256 carried by
-// the widened codes is removed once, at the final store.
+// Epilogue: per 16x16 tile and group, y += (sa[m]*sw[n]) * acc[m][n] on the
+// vector unit: one multiply, one int->float conversion and one FMA per
+// element and group (the scales are staged in LDS as fp32; a lane reads the
+// four token scales of its rows as one 16-byte read).  Measured on this
+// part, the multiply costs less issue time than forming the tile's outer
+// product of scales on the matrix core.  The factor 256 carried by the
+// widened codes is removed once, at the final store.
 //
 // Pipeline: group g passes through register buffer g%2 and LDS stage g%2.
 // While the waves compute group j from LDS, the loads of groups j+1 and j+2
@@ -45,7 +44,6 @@ namespace mq {
 namespace {
 
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef short v4s __attribute__((ext_vector_type(4)));
 
 constexpr int TBM = 256;    // tokens per tile
 constexpr int TBN = 128;    // output channels per tile
@@ -81,53 +79,16 @@ struct Stage {
 
 // LDS access through 32-bit LDS addresses, so that constant offsets fold
 // into the instructions' offset fields.
-typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) v4i lds_v4i;
-typedef __attribute__((address_space(3))) v2u lds_v2u;
+typedef __attribute__((address_space(3))) float lds_f32;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 __device__ __forceinline__ v4i lds_ld16(uint32_t a) { return *(const lds_v4i*)(uintptr_t)a; }
-__device__ __forceinline__ uint2 lds_ld8(uint32_t a) {
-  const v2u v = *(const lds_v2u*)(uintptr_t)a;
-  return make_uint2(v.x, v.y);
-}
 __device__ __forceinline__ void lds_st16(uint32_t a, v4i v) { *(lds_v4i*)(uintptr_t)a = v; }
-__device__ __forceinline__ void lds_st16u(uint32_t a, uint4 v) {
-  const v4i w = {(int)v.x, (int)v.y, (int)v.z, (int)v.w};
-  *(lds_v4i*)(uintptr_t)a = w;
-}
-
-__device__ __forceinline__ v4f mfma_scale(v4s a, v4s b) {
-  const v4f z = {0.f, 0.f, 0.f, 0.f};
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, z, 0, 0, 0);
-}
-
-__device__ __forceinline__ uint32_t bf16_trunc(float f) { return __float_as_uint(f) & 0xFFFF0000u; }
-
-// Scale-product operands, one 16-byte slot per token row / channel.  A lane
-// in chunk 0 reads the first 8 bytes (k slots 0-3), chunk 1 the last 8
-// (k slots 4-7); chunks 2-3 supply zeros.
-//   token:   {a1,a1, a2,a2 | a3,a3, 0,0}   with sa = a1 + a2 + a3 exactly
-//   channel: {w1,w2, w1,w2 | w1,w2, 0,0}   with s  = w1 + w2 exactly
-// Truncating to 8 significant bits leaves a remainder of at most 16 bits,
-// and its truncation one of at most 8, so the parts are exact.
-__device__ __forceinline__ uint4 token_scale_slot(float s) {
-  const uint32_t a1 = bf16_trunc(s);
-  const float r1 = s - __uint_as_float(a1);
-  const uint32_t a2 = bf16_trunc(r1);
-  const uint32_t a3 = bf16_trunc(r1 - __uint_as_float(a2));
-  return make_uint4((a1 >> 16) | a1, (a2 >> 16) | a2, (a3 >> 16) | a3, 0u);
-}
-
-__device__ __forceinline__ uint4 channel_scale_slot(uint16_t hbits) {
-  const float s = h2f(hbits);
-  const uint32_t w1 = bf16_trunc(s);
-  const uint32_t w2 = bf16_trunc(s - __uint_as_float(w1));
-  const uint32_t v = (w1 >> 16) | w2;
-  return make_uint4(v, v, v, 0u);
-}
+__device__ __forceinline__ float lds_ldf(uint32_t a) { return *(const lds_f32*)(uintptr_t)a; }
+__device__ __forceinline__ void lds_stf(uint32_t a, float v) { *(lds_f32*)(uintptr_t)a = v; }
 
 template <int BLK, bool DUMP>
 __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
@@ -258,12 +219,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
     lds_st16(b + C::OPB, widen8(S.R.x, S.R.y));
     lds_st16(b + C::OPB + 256, widen8(S.R.z, S.R.w));
     if (wave < 4) {
-      lds_st16u(st + C::SA_OFF + (uint32_t)tid * 16,
-                token_scale_slot((m0 + tid < a.M) ? __uint_as_float(S.sc) : 0.f));
+      lds_stf(st + C::SA_OFF + (uint32_t)tid * 4, (m0 + tid < a.M) ? __uint_as_float(S.sc) : 0.f);
     } else if (wave < 6) {
-      lds_st16u(st + C::SW_OFF + (uint32_t)(tid - 256) * 16, channel_scale_slot((uint16_t)S.sc));
+      lds_stf(st + C::SW_OFF + (uint32_t)(tid - 256) * 4, h2f((uint16_t)S.sc));
     }
-    if (tid < C::NSRS) lds_st16u(st + C::SR_OFF + (uint32_t)tid * 16, channel_scale_slot((uint16_t)S.sr));
+    if (tid < C::NSRS) lds_stf(st + C::SR_OFF + (uint32_t)tid * 4, h2f((uint16_t)S.sr));
   };
 
   const int wm = wave >> 1, wn = wave & 1;  // 64-row x 64-channel quarter of the tile
@@ -278,20 +238,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
   // The scale MFMA sums k slots 0-15; slots 8-15 (lanes 32-63) must add
   // nothing.  Only the channel side is zeroed there: the token side holds
   // finite values, and finite x 0 = 0.
-  const uint32_t chan_mask = ch < 2 ? 0xFFFFFFFFu : 0u;
-  const uint32_t scale_off = (uint32_t)(ch & 1) * 8;
-
   // One tile step: its MFMAs first, then the previous tile's epilogue (whose
   // products finished during the MFMAs), then a fence for the scheduler.
   auto tile_order = [](bool with_epi) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);  // MFMA
-    if (with_epi) __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);  // VALU
+    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+    if (with_epi) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);  // VALU
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  auto epi = [](float (&yt)[4], const v4f& P, const v4i& acc) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) yt[e] = fmaf(P[e], (float)acc[e], yt[e]);
+  // y += (sa[m] * s) * acc: the scale product on the vector unit (one
+  // multiply per element, cheaper here than a matrix-core step per tile)
+  auto epi = [](float (&yt)[4], const float4& sa4, float s, const v4i& acc) {
+    yt[0] = fmaf(sa4.x * s, (float)acc[0], yt[0]);
+    yt[1] = fmaf(sa4.y * s, (float)acc[1], yt[1]);
+    yt[2] = fmaf(sa4.z * s, (float)acc[2], yt[2]);
+    yt[3] = fmaf(sa4.w * s, (float)acc[3], yt[3]);
   };
 
   // residual-table lookups of this wave for group j: lane q*NBC + c holds
@@ -307,30 +268,26 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
     // the per-tile LDS addresses and fold into the instructions' offsets.
     uint32_t la = st + C::A_OFF + (uint32_t)lane * 16u + (uint32_t)wm * 8192u;
     uint32_t lb = st + C::B_OFF + (uint32_t)lane * 16u + (uint32_t)wn * 8192u;
-    uint32_t sa_b = st + C::SA_OFF + (uint32_t)r16 * 16u + scale_off + (uint32_t)wm * 1024u;
-    uint32_t sw_b = st + C::SW_OFF + (uint32_t)r16 * 16u + scale_off + (uint32_t)wn * 1024u;
+    uint32_t sa_b = st + C::SA_OFF + (uint32_t)ch * 16u + (uint32_t)wm * 256u;
+    uint32_t sw_b = st + C::SW_OFF + (uint32_t)r16 * 4u + (uint32_t)wn * 256u;
     asm volatile("" : "+v"(la), "+v"(lb), "+v"(sa_b), "+v"(sw_b));
     // tab is zero-filled and always allocated, so the read needs no guard;
     // the ballot is taken after the first column's tiles, by when it has
     // arrived
     const int ent_raw = (int)tab[tidx + j * C::NBC];
     v4i A0[4], A1[4];
-    v4s sa_op[4];
+    float4 sa4[4];  // sa of the lane's four tokens in each 16-row tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       A0[i] = lds_ld16(la + (i * 2 + 0) * 1024);
       A1[i] = lds_ld16(la + (i * 2 + 1) * 1024);
-      sa_op[i] = __builtin_bit_cast(v4s, lds_ld8(sa_b + i * 256));
+      sa4[i] = __builtin_bit_cast(float4, lds_ld16(sa_b + i * 64));
     }
     int ent_l = 0;
     uint64_t pres = 0;
-    auto chan_op = [&](uint32_t addr) {
-      const uint2 v = lds_ld8(addr);
-      return __builtin_bit_cast(v4s, make_uint2(v.x & chan_mask, v.y & chan_mask));
-    };
     v4i Bn0 = lds_ld16(lb);
     v4i Bn1 = lds_ld16(lb + 1024);
-    uint2 swn = lds_ld8(sw_b);
+    float swn = lds_ldf(sw_b);
     // Per 16-channel column q: the dense tiles run as a two-deep software
     // pipeline (the MFMAs of tile i are issued before the epilogue of tile
     // i-1), so at most two tiles' products are live.
@@ -338,23 +295,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
     for (int q = 0; q < 4; ++q) {
       const int tn = wn * 4 + q;
       const v4i B0 = Bn0, B1 = Bn1;
-      const v4s sw_op = __builtin_bit_cast(v4s, make_uint2(swn.x & chan_mask, swn.y & chan_mask));
+      const float swq = swn;
       if (q < 3) {  // next column's operands
         Bn0 = lds_ld16(lb + ((q + 1) * 2 + 0) * 1024);
         Bn1 = lds_ld16(lb + ((q + 1) * 2 + 1) * 1024);
-        swn = lds_ld8(sw_b + (q + 1) * 256);
+        swn = lds_ldf(sw_b + (q + 1) * 64);
       }
       v4i acc[4];
-      v4f P[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const v4i h0 = mfma(A0[i], B0, zero);
-        P[i] = mfma_scale(sa_op[i], sw_op);
         acc[i] = mfma(A1[i], B1, h0);
-        if (i > 0) epi(y[i - 1][q], P[i - 1], acc[i - 1]);
+        if (i > 0) epi(y[i - 1][q], sa4[i - 1], swq, acc[i - 1]);
         tile_order(i > 0);
       }
-      epi(y[3][q], P[3], acc[3]);
+      epi(y[3][q], sa4[3], swq, acc[3]);
       if (q == 0) {
         ent_l = tvalid ? ent_raw : 0;
         pres = __builtin_amdgcn_ballot_w64(ent_l > 0);
@@ -378,7 +333,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
         for (int c = 0; c < C::NBC; ++c) {
           if (!((pres >> (q * C::NBC + c)) & 1u)) continue;
           // (rare path: the residual addresses are formed here)
-          const v4s sr_op = chan_op(st + C::SR_OFF + (uint32_t)((tn * 16 + r16) * C::NBC + c) * 16 + scale_off);
+          const float srq = lds_ldf(st + C::SR_OFF + (uint32_t)((tn * 16 + r16) * C::NBC + c) * 4);
           const uint32_t lr = st + C::R_OFF + (uint32_t)lane * 16u + (uint32_t)tn * 2048u;
           const v4i R0 = lds_ld16(lr);
           const v4i R1 = lds_ld16(lr + 1024);
@@ -395,11 +350,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
               const v4i Rm = ((c < 2) ? R0 : R1) & msk;
               acc[i] = mfma((c < 2) ? A0[i] : A1[i], Rm, zero);
             }
-            P[i] = mfma_scale(sa_op[i], sr_op);
-            if (i > 0) epi(y[i - 1][q], P[i - 1], acc[i - 1]);
+            if (i > 0) epi(y[i - 1][q], sa4[i - 1], srq, acc[i - 1]);
             __builtin_amdgcn_sched_barrier(0);
           }
-          epi(y[3][q], P[3], acc[3]);
+          epi(y[3][q], sa4[3], srq, acc[3]);
           if (DUMP) {
             const int ent = __builtin_amdgcn_readlane(ent_l, q * C::NBC + c);
             const int64_t e_g = rp_row[rb] + ent - 1;
