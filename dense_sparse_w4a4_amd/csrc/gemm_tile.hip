@@ -4,14 +4,14 @@
 // compensation and the scale/reduce-sum epilogue, the residual reusing the
 // activation tile of the dense product.
 //
-// Tile: 128 tokens x 128 output channels per workgroup of four waves (2 x 2,
+// Tile: 256 tokens x 128 output channels per workgroup of eight waves (4 x 2,
 // 64 x 64 each, sixteen 16x16 MFMA tiles per wave).  One K step is one
 // 128-channel group.  Per group the workgroup stages, through a register
 // buffer into LDS:
-//   A  activation codes, 128 rows x 64 bytes
+//   A  activation codes, 256 rows x 64 bytes
 //   B  weight codes,     128 rows x 64 bytes
-//   R  residual codes for the same 128 channels (zero where no block is
-//      selected), 128 rows x 64 bytes
+//   R  residual codes of the block columns selected in these 128 channels,
+//      128 rows x 64 bytes (rows of unselected blocks hold unused data)
 //   the activation scales, weight scales and residual row scales.
 // Codes are widened to int8 once, while being written to LDS, and LDS holds
 // each MFMA operand in lane order (slot = (tile*2 + half)*64 + lane, 16
@@ -235,10 +235,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) y[i][q][e] = 0.f;
   const v4i zero = {0, 0, 0, 0};
-  // The scale MFMA sums k slots 0-15; slots 8-15 (lanes 32-63) must add
-  // nothing.  Only the channel side is zeroed there: the token side holds
-  // finite values, and finite x 0 = 0.
-  // One tile step: its MFMAs first, then the previous tile's epilogue (whose
+  // One tile step: its MFMAs first, then an earlier tile's epilogue (whose
   // products finished during the MFMAs), then a fence for the scheduler.
   auto tile_order = [](bool with_epi) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
@@ -272,61 +269,69 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
     uint32_t sw_b = st + C::SW_OFF + (uint32_t)r16 * 4u + (uint32_t)wn * 256u;
     asm volatile("" : "+v"(la), "+v"(lb), "+v"(sa_b), "+v"(sw_b));
     // tab is zero-filled and always allocated, so the read needs no guard;
-    // the ballot is taken after the first column's tiles, by when it has
-    // arrived
-    const int ent_raw = (int)tab[tidx + j * C::NBC];
+    // its value is first used after the dense tiles
+    int ent_raw = (int)tab[tidx + j * C::NBC];
+    // operands in the order the first tiles need them
+    v4i Bc0 = lds_ld16(lb), Bc1 = lds_ld16(lb + 1024);
     v4i A0[4], A1[4];
-    float4 sa4[4];  // sa of the lane's four tokens in each 16-row tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       A0[i] = lds_ld16(la + (i * 2 + 0) * 1024);
       A1[i] = lds_ld16(la + (i * 2 + 1) * 1024);
-      sa4[i] = __builtin_bit_cast(float4, lds_ld16(sa_b + i * 64));
     }
-    int ent_l = 0;
-    uint64_t pres = 0;
-    v4i Bn0 = lds_ld16(lb);
-    v4i Bn1 = lds_ld16(lb + 1024);
-    float swn = lds_ldf(sw_b);
-    // Per 16-channel column q: the dense tiles run as a two-deep software
-    // pipeline (the MFMAs of tile i are issued before the epilogue of tile
-    // i-1), so at most two tiles' products are live.
+    float4 sa4[4];  // sa of the lane's four tokens in each 16-row tile
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int tn = wn * 4 + q;
-      const v4i B0 = Bn0, B1 = Bn1;
-      const float swq = swn;
-      if (q < 3) {  // next column's operands
-        Bn0 = lds_ld16(lb + ((q + 1) * 2 + 0) * 1024);
-        Bn1 = lds_ld16(lb + ((q + 1) * 2 + 1) * 1024);
-        swn = lds_ldf(sw_b + (q + 1) * 64);
-      }
-      v4i acc[4];
+    for (int i = 0; i < 4; ++i) sa4[i] = __builtin_bit_cast(float4, lds_ld16(sa_b + i * 64));
+    float sw[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v4i h0 = mfma(A0[i], B0, zero);
-        acc[i] = mfma(A1[i], B1, h0);
-        if (i > 0) epi(y[i - 1][q], sa4[i - 1], swq, acc[i - 1]);
-        tile_order(i > 0);
-      }
-      epi(y[3][q], sa4[3], swq, acc[3]);
-      if (q == 0) {
-        ent_l = tvalid ? ent_raw : 0;
-        pres = __builtin_amdgcn_ballot_w64(ent_l > 0);
-      }
+    for (int q = 0; q < 4; ++q) sw[q] = lds_ldf(sw_b + q * 64);
+    v4i Bn0 = lds_ld16(lb + 2048), Bn1 = lds_ld16(lb + 3072);
+
+    // Dense tiles t = 4q + i (column q, row tile i) as one software
+    // pipeline: the MFMAs of tile t are issued before the epilogue of tile
+    // t-2, so three tiles' products are live at most.
+    v4i acc[16];
+    auto finish = [&](int t) {
+      const int q = t >> 2, i = t & 3;
+      epi(y[i][q], sa4[i], sw[q], acc[t]);
       if (DUMP) {
-        const int64_t n = n0 + tn * 16 + r16;
+        const int64_t n = n0 + (wn * 4 + q) * 16 + r16;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t m = m0 + (wm * 4 + i) * 16 + 4 * ch + e;
-            if (m < a.M && n < a.N) a.acc_dump[(m * a.N + n) * G + j] = acc[i][e] >> 8;
-          }
+        for (int e = 0; e < 4; ++e) {
+          const int64_t m = m0 + (wm * 4 + i) * 16 + 4 * ch + e;
+          if (m < a.M && n < a.N) a.acc_dump[(m * a.N + n) * G + j] = acc[t][e] >> 8;
+        }
       }
-      // zipper: residual blocks of these 16 channels in group j, against
-      // the same activation operands
-      if ((pres >> (q * C::NBC)) & ((1u << C::NBC) - 1u)) {
+    };
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int q = t >> 2, i = t & 3;
+      if (i == 0 && q > 0) {  // next column; prefetch the one after
+        Bc0 = Bn0;
+        Bc1 = Bn1;
+        if (q < 3) {
+          Bn0 = lds_ld16(lb + ((q + 1) * 2 + 0) * 1024);
+          Bn1 = lds_ld16(lb + ((q + 1) * 2 + 1) * 1024);
+        }
+      }
+      acc[t] = mfma(A1[i], Bc1, mfma(A0[i], Bc0, zero));
+      if (t >= 2) finish(t - 2);
+      tile_order(t >= 2);
+    }
+    finish(14);
+    finish(15);
+
+    // zipper: residual blocks of the wave's columns in group j, against the
+    // same activation operands (lane q*NBC + c of the ballot: column q,
+    // block column c)
+    asm volatile("" : "+v"(ent_raw));
+    const int ent_l = tvalid ? ent_raw : 0;
+    const uint64_t pres = __builtin_amdgcn_ballot_w64(ent_l > 0);
+    if (pres) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (!((pres >> (q * C::NBC)) & ((1u << C::NBC) - 1u))) continue;
+        const int tn = wn * 4 + q;
         const int nt = (int)((n0 + tn * 16) / BLK);
         const int rb = nt - nt0;
 #pragma unroll
@@ -337,23 +342,23 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
           const uint32_t lr = st + C::R_OFF + (uint32_t)lane * 16u + (uint32_t)tn * 2048u;
           const v4i R0 = lds_ld16(lr);
           const v4i R1 = lds_ld16(lr + 1024);
+          v4i racc[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             if (BLK == 128) {
-              acc[i] = mfma(A0[i], R0, zero);
-              acc[i] = mfma(A1[i], R1, acc[i]);
+              racc[i] = mfma(A1[i], R1, mfma(A0[i], R0, zero));
             } else if (BLK == 64) {
-              acc[i] = (c == 0) ? mfma(A0[i], R0, zero) : mfma(A1[i], R1, zero);
+              racc[i] = (c == 0) ? mfma(A0[i], R0, zero) : mfma(A1[i], R1, zero);
             } else {
               // 32-wide block c: MFMA half c/2, lane chunks 2*(c%2), 2*(c%2)+1
               const int msk = ((ch >> 1) == (c & 1)) ? -1 : 0;
               const v4i Rm = ((c < 2) ? R0 : R1) & msk;
-              acc[i] = mfma((c < 2) ? A0[i] : A1[i], Rm, zero);
+              racc[i] = mfma((c < 2) ? A0[i] : A1[i], Rm, zero);
             }
-            if (i > 0) epi(y[i - 1][q], sa4[i - 1], srq, acc[i - 1]);
+            if (i > 0) epi(y[i - 1][q], sa4[i - 1], srq, racc[i - 1]);
             __builtin_amdgcn_sched_barrier(0);
           }
-          epi(y[3][q], sa4[3], srq, acc[3]);
+          epi(y[3][q], sa4[3], srq, racc[3]);
           if (DUMP) {
             const int ent = __builtin_amdgcn_readlane(ent_l, q * C::NBC + c);
             const int64_t e_g = rp_row[rb] + ent - 1;
@@ -363,7 +368,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const int64_t m = m0 + (wm * 4 + i) * 16 + 4 * ch + e;
-                if (m < a.M) a.acc_dump[a.M * a.N * G + (e_g * a.M + m) * BLK + rr] = acc[i][e] >> 8;
+                if (m < a.M) a.acc_dump[a.M * a.N * G + (e_g * a.M + m) * BLK + rr] = racc[i][e] >> 8;
               }
           }
         }

@@ -279,6 +279,61 @@ def test_split_k_without_workspace_matches():
     assert_y_close(y_one, y_ref)
 
 
+def _gemm_without_workspace(qa, sa, layer, M, dump=False):
+    """mq_fused_gemm with no workspace (the tile kernel then makes one pass over K)."""
+    N, K, b, ns = layer.N, layer.K, layer.block, layer.n_select
+    y = torch.empty((M, N), dtype=torch.float16, device=qa.device)
+    acc = None
+    if dump:
+        acc = torch.empty(M * N * (K // 128) + ns * M * b, dtype=torch.int32, device=qa.device)
+    st = ops._check("mq_fused_gemm", ops.lib().mq_fused_gemm(
+        ops._ptr(qa), ops._ptr(sa), M, N, K, ops._ptr(layer.qw), ops._ptr(layer.sw), b, ns,
+        ops._ptr(layer.row_ptr) if ns else None, ops._ptr(layer.col_idx) if ns else None,
+        ops._ptr(layer.qr) if ns else None, ops._ptr(layer.sr) if ns else None,
+        ops._ptr(y), N, None, 0, ops.FLAG_DUMP_ACC if dump else 0, ops._ptr(acc),
+        ops._stream(None)))
+    assert st is None
+    return y, acc
+
+
+@pytest.mark.parametrize("M,b", [(290, 32), (290, 64), (290, 128), (16, 64), (3, 32)])
+def test_full_nibble_range(M, b):
+    # codes over the whole nibble range [-8, 7] on every operand (the
+    # quantisers stop at +-7), extreme rows and channels at -8: exact
+    # accumulators through the tile kernel with split-K (workspace) and in one
+    # pass (none), and through the streaming kernel for small M
+    N, K = 256, 2048
+    rng = np.random.default_rng(b + M)
+    qa_codes = rng.integers(-8, 8, size=(M, K)).astype(np.int8)
+    qa_codes[:2] = -8
+    qw_codes = rng.integers(-8, 8, size=(N, K)).astype(np.int8)
+    qw_codes[:16] = -8
+    KT = K // b
+    nsel = (N // b) * KT // 3
+    sel = np.sort(rng.choice((N // b) * KT, size=nsel, replace=False)).astype(np.int32)
+    row_ptr, col_idx = oracle.build_csr(sel, N, K, b)
+    qr = rng.integers(0, 256, size=(nsel, b, b // 2)).astype(np.uint8)
+    ref = dict(qw=oracle.slab_layout(oracle.pack_nibbles(qw_codes)),
+               sw=(rng.random((N, K // 128)) * 0.02 + 1e-3).astype(np.float16),
+               row_ptr=row_ptr, col_idx=col_idx, qr=qr,
+               sr=(rng.random((nsel, b)) * 0.01 + 1e-4).astype(np.float16), block=b, N=N, K=K)
+    sa_h = (rng.random((M, K // 128)) * 0.5 + 0.01).astype(np.float32)
+    y_ref, acc_ref, res_ref = oracle.fused_gemm(qa_codes, sa_h, ref)
+    layer = ops.PackedLayer(N, K, b, dev(ref["qw"]), dev(ref["sw"]), dev(row_ptr), dev(col_idx),
+                            dev(qr), dev(ref["sr"]))
+    qa, sa = dev(oracle.pack_nibbles(qa_codes)), dev(sa_h)
+    if M > 32:
+        assert ops.fused_gemm_workspace(M, N, K) > 0  # split-K with the workspace
+    y, base, res = ops.fused_gemm(qa, sa, layer, dump=True)
+    y1, acc1 = _gemm_without_workspace(qa, sa, layer, M, dump=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(base).astype(np.int64), acc_ref)
+    assert np.array_equal(host(res).astype(np.int64), np.stack(res_ref))
+    assert torch.equal(torch.cat([base.reshape(-1), res.reshape(-1)]), acc1)
+    assert_y_close(y, y_ref)
+    assert_y_close(y1, y_ref)
+
+
 @pytest.mark.parametrize("M,b", [(16, 64), (300, 32), (70, 128)])
 def test_unfused_ablation_matches(M, b):
     # dense-only fused GEMM followed by the standalone residual kernel gives
