@@ -125,9 +125,57 @@ def traffic(fetch_dir: str, write_dir: str, workload: str, kernel: str, cmd: str
     }
 
 
+# MI355X: 256 compute units of 4 SIMDs, in 8 XCDs of 4 shader engines.
+N_SIMD = 1024
+N_SE = 32
+
+
+def sq(dirs, workload: str, kernel: str, cmd: str) -> str:
+    """Per-dispatch means of SQ counters for one kernel, with derived shares.
+
+    SQ_BUSY_CYCLES is summed over shader engines (kernel cycles = value /
+    N_SE); SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES over SIMDs
+    (cycles); SQ_WAVE_CYCLES, SQ_WAIT_*, SQ_ACTIVE_INST_* over waves, in
+    units of 4 cycles."""
+    vals = defaultdict(list)
+    for d in dirs:
+        for r in csv.DictReader(open(_one(os.path.join(d, "*counter_collection.csv")))):
+            if kernel in r["Kernel_Name"]:
+                vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no dispatch of a kernel containing '{kernel}'")
+    m = {k: sum(v) / len(v) for k, v in vals.items()}
+    out = [f"# SQ counters, `{kernel}`, workload {workload}", "", "Commands (from the repository root on the GPU host):", "",
+           "```", cmd, "```", "",
+           "| counter | mean per dispatch | dispatches |", "|---|---:|---:|"]
+    for k in sorted(m):
+        out.append(f"| {k} | {m[k]:.0f} | {len(vals[k])} |")
+    out += ["", "Derived (MI355X: 1024 SIMDs, 32 shader engines):", ""]
+    if "SQ_BUSY_CYCLES" in m:
+        cyc = m["SQ_BUSY_CYCLES"] / N_SE
+        out.append(f"- kernel cycles (SQ_BUSY_CYCLES / 32): {cyc:.0f}")
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+            out.append(f"- matrix-core busy share per SIMD: {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (N_SIMD * cyc):.1%}")
+        if "SQ_ACTIVE_INST_VALU" in m:
+            out.append(f"- vector-unit issue share per SIMD (ACTIVE_INST_VALU x 4 cycles, MFMA issue included): "
+                       f"{4 * m['SQ_ACTIVE_INST_VALU'] / (N_SIMD * cyc):.1%}")
+    if "SQ_VALU_MFMA_COEXEC_CYCLES" in m and "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+        out.append(f"- matrix-core busy cycles with vector work co-issued: "
+                   f"{m['SQ_VALU_MFMA_COEXEC_CYCLES'] / m['SQ_VALU_MFMA_BUSY_CYCLES']:.1%}")
+    if "SQ_WAVE_CYCLES" in m:
+        w = m["SQ_WAVE_CYCLES"]
+        for k, what in (("SQ_ACTIVE_INST_ANY", "issuing"), ("SQ_WAIT_ANY", "waiting on a counter (s_waitcnt)"),
+                        ("SQ_WAIT_INST_ANY", "instruction ready but not issued")):
+            if k in m:
+                out.append(f"- wave time {what}: {m[k] / w:.1%}")
+    return "\n".join(out) + "\n"
+
+
 def main(argv):
     if len(argv) >= 5 and argv[0] == "stats":
         sys.stdout.write(stats(argv[1], argv[2], argv[3], argv[4]))
+    elif len(argv) >= 5 and argv[0] == "sq":
+        sys.stdout.write(sq(argv[1:-3], argv[-3], argv[-2], argv[-1]))
     elif len(argv) >= 6 and argv[0] == "traffic":
         json.dump(traffic(argv[1], argv[2], argv[3], argv[4], argv[5]), sys.stdout, indent=1)
         sys.stdout.write("\n")
