@@ -37,7 +37,9 @@
 // While the waves compute group j from LDS, the loads of groups j+1 and j+2
 // are in flight; each group's loads have about two compute steps to arrive.
 // Every step issues the same loads (groups past the end re-read the last
-// group), so the hardware load counters are waited on exactly.
+// group), so the hardware load counters are waited on exactly.  Within a
+// group, a wave's 16 dense tiles run as one software pipeline (the MFMAs of
+// tile t, then the epilogue of tile t-2), and its residual blocks follow.
 #include "gemm_common.h"
 
 namespace mq {
