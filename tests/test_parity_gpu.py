@@ -44,7 +44,9 @@ def _check_act(x16: np.ndarray, ldx_pad: int = 0):
 
 
 @pytest.mark.parametrize("M,K,pad", [(1, 128, 0), (5, 512, 8), (16, 4096, 0), (17, 14336, 0),
-                                     (300, 1024, 64)])
+                                     (300, 1024, 64),
+                                     # prefill sizes, a padded row stride
+                                     (1025, 4096, 0), (2048, 4096, 8)])
 def test_act_quant_bit_exact(M, K, pad):
     spec = syn.LayerSpec("t", K=K, N=128)
     _check_act(syn.make_acts(spec, M, seed=M), pad)
