@@ -79,5 +79,7 @@ def test_full_size_qwen3_32b(K, N):
     _check(syn.qwen3_32b(K, N), [1, 16, 4096])
 
 
-def test_full_size_llama3_70b_ffn():
-    _check(syn.llama3_70b(64, 0.10), [syn.LLAMA3_70B_M])
+@pytest.mark.parametrize("b,rho", [(32, 0.20), (64, 0.10), (128, 0.05)])
+def test_full_size_llama3_70b_ffn(b, rho):
+    # every block size of the Llama-3-70B grid, at a budget from its range
+    _check(syn.llama3_70b(b, rho), [syn.LLAMA3_70B_M])
