@@ -480,6 +480,23 @@ def main():
     roof["avg_launch_us"] = round(gemm_time_s / launches * 1e6, 3)
     roof["alg_bytes_per_launch"] = per_step_gemm_bytes / launches
     roof["alg_ops_per_launch"] = per_step_ops / launches
+    if bound == "hbm":
+        # a plain device copy measured here (outside the timed region): the
+        # rate a streaming kernel reaches on this part, beside the datasheet peak
+        a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        c0.record()
+        for _ in range(10):
+            b.copy_(a)
+        c1.record()
+        torch.cuda.synchronize()
+        copy_gbs = 2 * a.numel() / (c0.elapsed_time(c1) * 1e-3 / 10) / 1e9
+        roof["measured_copy_gbs"] = round(copy_gbs, 1)
+        roof["frac_of_copy"] = round(achieved / copy_gbs, 4)
+        del a, b
 
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

@@ -49,6 +49,17 @@ def _short(name: str) -> str:
     return name[:90]
 
 
+def _pct(v, q: float) -> float:
+    """q-th percentile (linear interpolation between order statistics)."""
+    v = sorted(v)
+    if len(v) == 1:
+        return v[0]
+    x = (len(v) - 1) * q / 100.0
+    i = int(x)
+    j = min(i + 1, len(v) - 1)
+    return v[i] + (v[j] - v[i]) * (x - i)
+
+
 def stats(outdir: str, prefix: str, title: str, cmd: str) -> str:
     rows = list(csv.DictReader(open(_one(os.path.join(outdir, f"{prefix}_kernel_stats.csv")))))
     trace = list(csv.DictReader(open(_one(os.path.join(outdir, f"{prefix}_kernel_trace.csv")))))
@@ -64,10 +75,12 @@ def stats(outdir: str, prefix: str, title: str, cmd: str) -> str:
             key = (_short(t["Kernel_Name"]), int(t["Grid_Size_X"]), int(t["Workgroup_Size_X"]))
             per[key].append((int(t["End_Timestamp"]) - int(t["Start_Timestamp"])) / 1e3)
     if per:
-        out += ["", "Fused GEMM launches by grid:", "", "| kernel | grid (threads) | block | calls | average (us) |",
-                "|---|---:|---:|---:|---:|"]
+        out += ["", "Fused GEMM launches by grid:", "",
+                "| kernel | grid (threads) | block | calls | average (us) | p10 / median / p90 (us) |",
+                "|---|---:|---:|---:|---:|---:|"]
         for (k, g, b), v in sorted(per.items()):
-            out.append(f"| `{k}` | {g} | {b} | {len(v)} | {sum(v) / len(v):.2f} |")
+            out.append(f"| `{k}` | {g} | {b} | {len(v)} | {sum(v) / len(v):.2f} | "
+                       f"{_pct(v, 10):.2f} / {_pct(v, 50):.2f} / {_pct(v, 90):.2f} |")
         # every template instance of a kernel together (the figure the
         # benchmark's per-launch average compares with)
         fam = defaultdict(list)
@@ -76,9 +89,10 @@ def stats(outdir: str, prefix: str, title: str, cmd: str) -> str:
                 if name in k:
                     fam[name] += v
         out += ["", "All launches per kernel (every template instance):", "",
-                "| kernel | calls | average (us) |", "|---|---:|---:|"]
+                "| kernel | calls | average (us) | p10 / median / p90 (us) |", "|---|---:|---:|---:|"]
         for name, v in sorted(fam.items()):
-            out.append(f"| `{name}` | {len(v)} | {sum(v) / len(v):.2f} |")
+            out.append(f"| `{name}` | {len(v)} | {sum(v) / len(v):.2f} | "
+                       f"{_pct(v, 10):.2f} / {_pct(v, 50):.2f} / {_pct(v, 90):.2f} |")
     return "\n".join(out) + "\n"
 
 
@@ -138,10 +152,15 @@ def sq(dirs, workload: str, kernel: str, cmd: str) -> str:
     (cycles); SQ_WAVE_CYCLES, SQ_WAIT_*, SQ_ACTIVE_INST_* over waves, in
     units of 4 cycles."""
     vals = defaultdict(list)
+    clocks = []  # (SQ_BUSY_CYCLES / N_SE) / dispatch duration, GHz
     for d in dirs:
         for r in csv.DictReader(open(_one(os.path.join(d, "*counter_collection.csv")))):
             if kernel in r["Kernel_Name"]:
                 vals[r["Counter_Name"]].append(float(r["Counter_Value"]))
+                if r["Counter_Name"] == "SQ_BUSY_CYCLES":
+                    ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                    if ns > 0:
+                        clocks.append(float(r["Counter_Value"]) / N_SE / ns)
     if not vals:
         raise SystemExit(f"no dispatch of a kernel containing '{kernel}'")
     m = {k: sum(v) / len(v) for k, v in vals.items()}
@@ -154,6 +173,9 @@ def sq(dirs, workload: str, kernel: str, cmd: str) -> str:
     if "SQ_BUSY_CYCLES" in m:
         cyc = m["SQ_BUSY_CYCLES"] / N_SE
         out.append(f"- kernel cycles (SQ_BUSY_CYCLES / 32): {cyc:.0f}")
+        if clocks:
+            out.append(f"- observed shader clock (kernel cycles / dispatch duration): "
+                       f"{_pct(clocks, 50):.2f} GHz median ({min(clocks):.2f}-{max(clocks):.2f})")
         if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
             out.append(f"- matrix-core busy share per SIMD: {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (N_SIMD * cyc):.1%}")
         if "SQ_ACTIVE_INST_VALU" in m:
