@@ -1,5 +1,6 @@
-"""The decode kernel's in-prologue activation quantiser forms v/s from the
-reciprocal of the scale and one fma correction instead of a division.  This
+"""The activation-quantisation kernel and the decode kernel's in-prologue
+quantiser form v/s from the reciprocal of the scale and one fma correction
+instead of a division.  This
 checks, exhaustively on the host, that the codes it gives equal those of the
 IEEE division the activation quantiser is defined with (code =
 clamp(rint(v / s), -7, 7), s = amax / 7 in fp32), for every fp16 amax and
