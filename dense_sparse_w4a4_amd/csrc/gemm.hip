@@ -67,8 +67,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int G = (int)(a.K / kGroup);
   float* sa_t = reinterpret_cast<float*>(smem);  // [G][16]: sa/256 of the tile's tokens
-  float* sw_t = sa_t + G * 16;                     // [G][CW]: weight scales of the tile's channels
-  float* spare = sw_t + G * CW;                    // [2]: target of stores past the tables
+  float* sw_t = sa_t + G * 16;                     // [G][CW+1]: weight scales of the tile's channels
+  float* spare = sw_t + G * (CW + 1);              // [2]: target of stores past the tables
   unsigned char* qa_t = smem + stream_qa_offset(G, NS);  // QP > 0: [M][qrow] activation codes
   const int qrow = (int)(a.K / 2) + 64;
   float* red = reinterpret_cast<float*>(smem);   // [KS][16][CW+1] after the streams
@@ -150,14 +150,14 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
       const uint4 X = QP > 0 ? lds_x(j) : D.X[u];
 #pragma unroll
       for (int s = 0; s < NS; ++s)
-        item(s, D.W[u][s], X, valid ? sw_t[j * CW + 16 * s + r16] : 0.f, 0xFFFFFFFFu, j, valid, 0,
+        item(s, D.W[u][s], X, valid ? sw_t[j * (CW + 1) + 16 * s + r16] : 0.f, 0xFFFFFFFFu, j, valid, 0,
              false);
     }
   };
 
   // ---- prologue: the tile's scale loads first, then two dense units and
   // the CSR window in flight; the scales go to LDS (transposed to [G][16]
-  // and [G][CW]) as soon as they arrive, without waiting for the units ----
+  // and [G][CW+1]) as soon as they arrive, without waiting for the units ----
   const int nunits = (ng + U - 1) / U;
   // QP > 0: the fp16 activations of the tile's (token, group) pairs, one
   // 16-byte load per pass and lane, all issued first (the launcher picks QP
@@ -183,8 +183,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
   for (int k = 0; k < SMAX; ++k) {
     if constexpr (QP == 0) {
-      const int i = min((int)threadIdx.x + k * 64 * KS, nsa - 1);
-      const int mm = i / G, j = i - mm * G;
+      // activation scales in table order (entry e = group * 16 + token), so
+      // consecutive lanes store to consecutive LDS words
+      const int e = min((int)threadIdx.x + k * 64 * KS, nsa - 1);
+      const int j = e >> 4, mm = e & 15;
       const int64_t m = m0 + mm;
       pa[k] = *reinterpret_cast<const float*>(sa_b + (uint32_t)(((m < a.M ? m : a.M - 1) * G + j) * 4));
     } else {
@@ -268,25 +270,25 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   // and the waits stay exact; with QP > 0 the activation scales of the
   // tile's tokens come from the quantisation below and only the padding
   // rows are written here)
-  auto stage_a = [&](int i, float v) {
-    const int mm = i / G, j = i - mm * G;
+  auto stage_a = [&](int e, float v) {  // e = group * 16 + token
+    const int mm = e & 15;
     const bool pad = m0 + mm >= a.M;
-    float* const da = i < nsa && (QP == 0 || pad) ? sa_t + j * 16 + mm : spare;
+    float* const da = e < nsa && (QP == 0 || pad) ? sa_t + e : spare;
     *da = pad ? 0.f : v * kInv256;
   };
-  auto stage_w = [&](int i, uint16_t w) {
+  auto stage_w = [&](int i, uint16_t w) {  // i = channel * G + group (source order)
     const int r = i / G, j = i - r * G;
-    float* const dw = i < nsw ? sw_t + j * CW + r : spare + 1;
+    float* const dw = i < nsw ? sw_t + j * (CW + 1) + r : spare + 1;
     *dw = h2f(w);
   };
 #pragma unroll
   for (int k = 0; k < SMAX; ++k) stage_a((int)threadIdx.x + k * 64 * KS, pa[k]);
 #pragma unroll
   for (int k = 0; k < WMAX; ++k) stage_w((int)threadIdx.x + k * 64 * KS, pw[k]);
-  for (int i = (int)threadIdx.x + SMAX * 64 * KS; i < nsa; i += 64 * KS) {  // long K only
-    const int mm = i / G, j = i - mm * G;
+  for (int e = (int)threadIdx.x + SMAX * 64 * KS; e < nsa; e += 64 * KS) {  // long K only
+    const int j = e >> 4, mm = e & 15;
     const int64_t m = m0 + mm;
-    stage_a(i, QP == 0 ? a.sa[(m < a.M ? m : a.M - 1) * G + j] : 0.f);
+    stage_a(e, QP == 0 ? a.sa[(m < a.M ? m : a.M - 1) * G + j] : 0.f);
   }
   for (int i = (int)threadIdx.x + WMAX * 64 * KS; i < nsw; i += 64 * KS)  // long K only
     stage_w(i, a.sw[(n0 + i / G) * G + i % G]);

@@ -128,8 +128,13 @@ struct GemmArgs {
 // 4 passes of the workgroup's 16-lane teams.
 constexpr int kStreamQuantRows = 4;
 // LDS byte offset of the streaming kernel's activation codes: after the
-// [G][16] activation and [G][16*ns] weight scale tables and the spare slots.
-__host__ __device__ constexpr int stream_qa_offset(int G, int ns) { return (64 + 64 * ns) * G + 16; }
+// [G][16] activation scale table, the [G][16*ns + 1] weight scale table
+// (rows padded by one slot so that the staging stores, which walk the groups
+// of one channel, fall in distinct LDS banks), rounded up to 16 bytes, and
+// the spare slots.
+__host__ __device__ constexpr int stream_qa_offset(int G, int ns) {
+  return 64 * G + (((16 * ns + 1) * G + 3) / 4) * 16 + 16;
+}
 // Launch shape of the streaming kernel: 16-channel slabs per workgroup,
 // waves per workgroup, groups per streamed unit, quantisation passes (0:
 // the activations arrive as codes).
