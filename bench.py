@@ -480,9 +480,11 @@ def main():
     roof["avg_launch_us"] = round(gemm_time_s / launches * 1e6, 3)
     roof["alg_bytes_per_launch"] = per_step_gemm_bytes / launches
     roof["alg_ops_per_launch"] = per_step_ops / launches
-    if bound == "hbm":
+    if bound == "hbm" and not args.copy_calibration:
         # a plain device copy measured here (outside the timed region): the
-        # rate a streaming kernel reaches on this part, beside the datasheet peak
+        # rate a streaming kernel reaches on this part, beside the datasheet
+        # peak (not in counter runs, whose 256 MiB calibration copy must stay
+        # the largest copy of the run)
         a = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
         for _ in range(3):
