@@ -121,6 +121,11 @@ def traffic(fetch_dir: str, write_dir: str, workload: str, kernel: str, cmd: str
     w_k = pick(write, kernel)
     ff = COPY_BYTES / (fc * 1024.0)
     fw = COPY_BYTES / (wc * 1024.0)
+    # the write counter reads a plain copy's bytes exactly on this part: any
+    # other factor means the largest copy of the run was not the calibration copy
+    if not 0.95 <= fw <= 1.05:
+        raise SystemExit(f"calibration copy not found: WRITE_SIZE of the largest copy is {wc:.0f} KiB, "
+                         f"expected {COPY_BYTES / 1024:.0f}")
     fetch_kib = sum(f_k) / len(f_k)
     write_kib = sum(w_k) / len(w_k)
     return {
