@@ -2,28 +2,38 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 
-One step is one pass of the online hot path - fp16 activations to fp16 y
-through mq_fused_layer (activation quantisation and the fused GEMM; one
-kernel for M <= 4, where the GEMM quantises the token tile itself, else the
-act-quant kernel then the fused GEMM) - for every (shape, M) of the
-workload, with inputs resident in HBM.  The offline part (Delta-score selection and packing) runs once on
-the GPU before timing.  Every (shape, M) in a step reads its own copy of the
-packed weights, and whole copies of the step's data rotate between steps so
-the footprint is >= 512 MB: the 256 MB Infinity Cache cannot serve weights
-from a previous launch.
+Default workload: the Qwen3-32B MLP shapes (K x N = 5120 x 25600 and
+25600 x 5120, 10% residual in 64 x 64 blocks) at M = 1, 16, 256 and 4096 -
+decode-shaped launches bounded by HBM and prefill-shaped launches bounded by
+the int8 matrix cores in one step.  One step is one pass of the online hot
+path - fp16 activations to fp16 y through mq_fused_layer (activation
+quantisation and the fused GEMM; one kernel where the GEMM quantises the
+token tile itself, else the act-quant kernel then the fused GEMM) - for every
+(shape, M) of the workload, with inputs resident in HBM.  The offline part
+(Delta-score selection and packing) runs once on the GPU before timing.
+Every (shape, M) in a step reads its own copy of the packed weights, and
+whole copies of the step's data rotate between steps so the footprint is
+>= 512 MB: the 256 MB Infinity Cache cannot serve weights from a previous
+launch.
 
 Printed JSON (one line on stdout):
-  value      algorithmic bytes of the step (fp16 X, packed layer, fp16 Y of
-             every (shape, M)) / step time (GB/s)
-  tops       algorithmic integer ops of the step / step time
-  roofline   the fused GEMM (dominant kernel): algorithmic bytes (decode) or
-             ops (prefill) per launch / average launch time, from HIP events
-             around K replays of a graph holding only the step's GEMM
-             launches (the one-kernel layer where M <= 4: its bytes count
-             the fp16 activations it reads instead of codes)
+  value      algorithmic integer ops of the step / step time (TOP/s)
+  gbs        algorithmic bytes of the step (fp16 X, packed layer, fp16 Y of
+             every (shape, M)) / step time
+  roofline   per GEMM kernel (streaming kernel for M <= 32, tile kernel
+             above), the dominant one (most time per step) first:
+             algorithmic bytes (streaming: HBM) or ops (tile: int8 MFMA) per
+             launch / average launch time, from HIP events around K replays
+             of a graph holding only that kernel's launches of the step (the
+             one-kernel layer where it applies: its bytes count the fp16
+             activations it reads instead of codes); next to the measured
+             int8 matrix-core rate, shader clock and device-copy rate
+  per_pair   per (shape, M): fused GEMM launch time p10 / median / p90 over
+             replays, TOPS, GB/s, roofline fractions, the same kernel with an
+             empty CSR (residual cost), act-quant alone, the whole layer
+  cpu_baseline  the CPU oracle (quantise + fused GEMM) on a bounded sample
 Launches are replayed from HIP graphs (one per rotating set) so the timed
 region measures the GPU, not Python launch overhead (--no-graph: eager).
-  cpu_baseline  the CPU oracle (quantise + fused GEMM) on a bounded sample
 """
 from __future__ import annotations
 
@@ -44,26 +54,39 @@ INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
 ROTATE_BYTES = 512 << 20
 
 
+DEFAULT_WORKLOAD = "qwen3-32b-sweep"
+PAIR_REPLAYS = 15   # timed replays per (shape, M) and mode
+
+
 def workload(name: str):
+    """[(LayerSpec, [M, ...]), ...] of a named workload."""
     from dense_sparse_w4a4_amd import synthetic as syn
+    if name == "qwen3-32b-sweep":
+        return [(syn.qwen3_32b(K, N), syn.QWEN3_32B_M) for (K, N) in syn.QWEN3_32B_SHAPES]
     if name == "llama3-8b-decode":
-        return [(syn.llama3_8b(K, N), syn.LLAMA3_8B_DECODE_M) for (K, N) in syn.LLAMA3_8B_SHAPES], "hbm"
+        return [(syn.llama3_8b(K, N), syn.LLAMA3_8B_DECODE_M) for (K, N) in syn.LLAMA3_8B_SHAPES]
     if name == "llama3-8b-prefill":
-        return [(syn.llama3_8b(K, N), [syn.LLAMA3_8B_PREFILL_M]) for (K, N) in syn.LLAMA3_8B_SHAPES], "mfma"
+        return [(syn.llama3_8b(K, N), [syn.LLAMA3_8B_PREFILL_M]) for (K, N) in syn.LLAMA3_8B_SHAPES]
     if name.startswith("qwen3-32b"):
         ms = {"qwen3-32b-decode": [1, 16], "qwen3-32b-256": [256], "qwen3-32b-4096": [4096]}.get(name)
         if ms is None:
             raise SystemExit(f"unknown workload {name}")
-        return [(syn.qwen3_32b(K, N), ms) for (K, N) in syn.QWEN3_32B_SHAPES], ("hbm" if max(ms) <= 16 else "mfma")
+        return [(syn.qwen3_32b(K, N), ms) for (K, N) in syn.QWEN3_32B_SHAPES]
     if name.startswith("llama3-70b"):
         # llama3-70b-b{32,64,128}-r{0,5,10,20}
         parts = name.split("-")
         b = int(parts[2][1:])
         rho = int(parts[3][1:]) / 100.0
-        return [(syn.llama3_70b(b, rho), [syn.LLAMA3_70B_M])], "mfma"
+        return [(syn.llama3_70b(b, rho), [syn.LLAMA3_70B_M])]
     if name == "tiny":
-        return [(syn.TINY, [syn.TINY_M])], "hbm"
+        return [(syn.TINY, [syn.TINY_M])]
     raise SystemExit(f"unknown workload {name}")
+
+
+def kernel_of(M: int) -> str:
+    """The GEMM kernel the library runs for M tokens (the streaming kernel up
+    to 32 tokens, the LDS-tiled kernel above)."""
+    return "gemm_stream_kernel" if M <= 32 else "gemm_tile_kernel"
 
 
 def weight_bytes(N, K, b, ns):
@@ -87,27 +110,28 @@ def gemm_ops(M, N, K, b, ns):
     return 2 * M * N * K + 2 * M * ns * b * b
 
 
-def traffic_from_profile(wname: str):
-    """HBM bytes per GEMM launch measured with rocprofv3 counters, if the
-    stored measurement was taken on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", f"traffic_{wname}.json")
+def traffic_from_profile(wname: str, kernel: str):
+    """HBM bytes per launch of `kernel` measured with rocprofv3 counters, if
+    the stored measurement was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{wname}.json")
     if not os.path.exists(p):
         return None
     d = json.load(open(p))
     from dense_sparse_w4a4_amd.profiling import kernel_sources_sha
-    if d.get("sources_sha") != kernel_sources_sha():
+    if d.get("sources_sha") != kernel_sources_sha() or d.get("kernel") != kernel:
         return None
     return d.get("bytes_per_launch")
 
 
-def cpu_baseline(layers, budget_s: float):
+def cpu_baseline(layers, budget_s: float, host_layers=None):
     """Time the oracle's online path (quantise + fused GEMM) on the workload.
 
-    The oracle's packed layers are built first (untimed).  Then whole passes
-    over every (shape, M) of the step are timed until about budget_s seconds
-    of CPU work have accumulated (at least one pass), so the sample is the
-    step itself, repeated; a pass that would exceed four budgets of wall time
-    stops early and the sample names what ran."""
+    The oracle's packed layers are built first (untimed).  Then the (shape, M)
+    pairs of the step are timed in order of increasing M, passes over all of
+    them repeated while under budget_s seconds; a pair is skipped once the
+    time so far plus an estimate of its own (ops x the slowest rate seen
+    yet) would pass twice the budget, so the sample stays bounded and names
+    what ran.  Rates are algorithmic ops (and bytes) over the oracle's time."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -116,34 +140,41 @@ def cpu_baseline(layers, budget_s: float):
         threads = os.cpu_count() or 1
     from dense_sparse_w4a4_amd import synthetic as syn
     prepared = []
-    for spec, ms in layers:
-        w = syn.make_weight(spec)
-        xc = syn.make_calib(spec)
+    for i, (spec, ms) in enumerate(layers):
+        w, xc = host_layers[i] if host_layers else (syn.make_weight(spec), syn.make_calib(spec))
         sel, _, _ = oracle.select_blocks(w, xc, spec.block, spec.n_select)
         packed = oracle.pack_weights(w, spec.block, sel)
         for M in ms:
-            prepared.append((spec, M, len(sel), packed, syn.make_acts(spec, M)))
-    tbytes, tops, tsec, passes, partial = 0, 0, 0.0, 0, []
+            prepared.append((spec, M, len(sel), packed))
+    prepared.sort(key=lambda p: p[1])
+    tbytes, tops, tsec, passes, ran, skipped = 0, 0, 0.0, 0, [], []
+    sec_per_op = 0.0
     while True:
-        for (spec, M, ns, packed, x) in prepared:
+        for (spec, M, ns, packed) in prepared:
+            ops_ = gemm_ops(M, spec.N, spec.K, spec.block, ns)
+            if tsec + ops_ * sec_per_op > 2 * budget_s:
+                if passes == 0:
+                    skipped.append(f"{spec.K}x{spec.N}@M={M}")
+                continue
+            x = syn.make_acts(spec, M)
             t0 = time.perf_counter()
             qa, sa = oracle.quantize_act(x)
             oracle.fused_gemm(qa, sa, packed)
-            tsec += time.perf_counter() - t0
+            dt = time.perf_counter() - t0
+            tsec += dt
+            sec_per_op = dt / ops_  # the rate improves with M: the last pair predicts the next
             tbytes += layer_bytes(M, spec.N, spec.K, spec.block, ns)
-            tops += gemm_ops(M, spec.N, spec.K, spec.block, ns)
+            tops += ops_
             if passes == 0:
-                partial.append(f"{spec.K}x{spec.N}@M={M}")
-            if tsec > 4 * budget_s:
-                break
+                ran.append(f"{spec.K}x{spec.N}@M={M}")
         passes += 1
-        if tsec >= budget_s or tsec > 4 * budget_s:
+        if tsec >= budget_s or not ran or passes >= 50:
             break
-    what = ", ".join(partial)
-    return dict(value=tbytes / tsec / 1e9, unit="GB/s", tops=tops / tsec / 1e12, cores=int(threads),
-                kind="oracle", seconds=round(tsec, 3),
-                sample=f"{passes} pass(es) of oracle quantize_act + fused_gemm (numpy; BLAS "
-                       f"threads = cores) over {what}")
+    return dict(value=round(tops / tsec / 1e12, 6), unit="TOP/s", gbs=round(tbytes / tsec / 1e9, 4),
+                cores=int(threads), kind="oracle", seconds=round(tsec, 3),
+                sample=f"{passes} pass(es) of oracle quantize_act + fused_gemm (numpy; BLAS threads = "
+                       f"cores) over {', '.join(ran)}"
+                       + (f"; not run (over the time bound): {', '.join(skipped)}" if skipped else ""))
 
 
 def sweep_llama3_70b(args):
@@ -258,16 +289,50 @@ def smooth_study(args):
                       "rows": rows}), flush=True)
 
 
+def _pct(v, q):
+    v = sorted(v)
+    if len(v) == 1:
+        return v[0]
+    x = (len(v) - 1) * q / 100.0
+    i = int(x)
+    j = min(i + 1, len(v) - 1)
+    return v[i] + (v[j] - v[i]) * (x - i)
+
+
+def measure_mfma_ceiling(torch, ops):
+    """The int8 matrix-core rate and shader clock measured on this device:
+    2 workgroups of 4 waves per compute unit, each wave issuing back-to-back
+    V_MFMA_I32_16X16X64_I8 (four independent chains), timed with HIP events;
+    the clock is the waves' shader-cycle count over the same wall time."""
+    blocks, iters = 512, 20000
+    ops.measure_mfma(blocks, 200)  # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    cycles, _ = ops.measure_mfma(blocks, iters)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3
+    total_ops = blocks * 4 * iters * 4 * 2 * 16 * 16 * 64
+    cyc = sorted(cycles.cpu().tolist())
+    return dict(measured_mfma_int8_tops=round(total_ops / t / 1e12, 1),
+                observed_clock_ghz=round(cyc[len(cyc) // 2] / t / 1e9, 3),
+                probe="512 workgroups x 4 waves, 20000 rounds of 4 independent v_mfma_i32_16x16x64_i8 each")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama3-8b-decode")
-    ap.add_argument("--cpu-budget", type=float, default=10.0)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying HIP graphs")
-    ap.add_argument("--per-shape", action="store_true", help="also time each (shape, M) on its own")
+    ap.add_argument("--no-per-pair", action="store_true",
+                    help="skip the per-(shape, M) launch statistics (counter runs)")
+    ap.add_argument("--ablation", action="store_true",
+                    help="per (shape, M) also time the unfused design (dense launch + standalone residual kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for HBM counter calibration)")
     ap.add_argument("--smooth", action="store_true",
@@ -298,15 +363,18 @@ def main():
         return
     dev = torch.device("cuda:0")
     ops.lib()
-    layers, bound = workload(args.workload)
+    layers = workload(args.workload)
     log = lambda *a: print(*a, file=sys.stderr, flush=True)  # noqa: E731
 
     # ---- offline: select + pack once per shape (GPU), then replicate ----
     t0 = time.perf_counter()
-    base = []
+    base, host_layers = [], []
     for spec, ms in layers:
-        wt = torch.from_numpy(syn.make_weight(spec)).to(dev)
-        xct = torch.from_numpy(syn.make_calib(spec)).to(dev)
+        w_np, xc_np = syn.make_weight(spec), syn.make_calib(spec)
+        if not args.no_cpu_baseline:
+            host_layers.append((w_np, xc_np))
+        wt = torch.from_numpy(w_np).to(dev)
+        xct = torch.from_numpy(xc_np).to(dev)
         sel, _, _ = ops.select_blocks(wt, xct, spec.block, spec.n_select)
         layer = ops.pack_weights(wt, spec.block, sel)
         xs = {M: torch.from_numpy(syn.make_acts(spec, M)).to(dev) for M in ms}
@@ -327,45 +395,59 @@ def main():
                 y = torch.empty((M, spec.N), dtype=torch.float16, device=dev)
                 wsb = ops.fused_layer_workspace(M, spec.N, spec.K)
                 ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-                s.append((spec, M, L, x, qa, sa, y, ws))
+                gwsb = ops.fused_gemm_workspace(M, spec.N, spec.K)
+                gws = torch.empty(max(gwsb, 1), dtype=torch.uint8, device=dev)
+                s.append((spec, M, L, x, qa, sa, y, ws, gws))
         sets.append(s)
     # pairs the layer runs as one kernel (the GEMM quantises the token tile)
     one_kernel = [ops.fused_layer_workspace(M, s.N, s.K) == 0 for s, M in pairs]
+    kern = [kernel_of(M) for _, M in pairs]
     torch.cuda.synchronize()
     log(f"[bench] workload {args.workload}: {len(pairs)} (shape, M) pairs per step, "
         f"{R} rotating copies x {step_footprint / 2**20:.1f} MiB, setup {time.perf_counter() - t0:.1f}s")
 
     per_step_bytes = sum(layer_bytes(M, s.N, s.K, s.block, s.n_select) for s, M in pairs)
-    per_step_gemm_bytes = sum((layer_bytes if one else gemm_bytes)(M, s.N, s.K, s.block, s.n_select)
-                              for (s, M), one in zip(pairs, one_kernel))
     per_step_ops = sum(gemm_ops(M, s.N, s.K, s.block, s.n_select) for s, M in pairs)
+    # the GEMM launch of a pair: the one-kernel layer (fp16 X in) or the fused
+    # GEMM from codes
+    launch_bytes = [(layer_bytes if one else gemm_bytes)(M, s.N, s.K, s.block, s.n_select)
+                    for (s, M), one in zip(pairs, one_kernel)]
+    launch_ops = [gemm_ops(M, s.N, s.K, s.block, s.n_select) for s, M in pairs]
 
-    def run_set(i, whole_layer=True):
-        # whole_layer: the step (mq_fused_layer); otherwise only the GEMM
-        # launches (the one-kernel layer where it applies, else the fused
-        # GEMM from precomputed codes)
-        for p_idx, (spec, M, L, x, qa, sa, y, ws) in enumerate(sets[i % R]):
-            if whole_layer or one_kernel[p_idx]:
+    def run_set(i, which=None):
+        # which=None: the step (mq_fused_layer for every pair); otherwise the
+        # GEMM launches of the pairs whose kernel is `which` (the one-kernel
+        # layer where it applies, else the fused GEMM from precomputed codes)
+        for p_idx, (spec, M, L, x, qa, sa, y, ws, gws) in enumerate(sets[i % R]):
+            if which is None:
                 ops.fused_layer(x, L, out=y, workspace=ws)
-            else:
-                ops.fused_gemm(qa, sa, L, out=y)
+            elif kern[p_idx] == which:
+                if one_kernel[p_idx]:
+                    ops.fused_layer(x, L, out=y, workspace=ws)
+                else:
+                    ops.fused_gemm(qa, sa, L, out=y, workspace=gws)
 
     for i in range(max(args.warmup, R)):
         run_set(i)
     torch.cuda.synchronize()
 
-    # One HIP graph per rotating set: the whole step (the layer for every
-    # (shape, M)), and the GEMM launches alone for per-launch timing.
+    classes = sorted(set(kern))
     use_graph = not args.no_graph
+    cap = torch.cuda.Stream()
     if use_graph:
-        g_step, g_gemm = [], []
-        cap = torch.cuda.Stream()
+        # one HIP graph per rotating set: the whole step, and per kernel the
+        # step's GEMM launches alone (per-launch timing)
+        g_step, g_cls = [], {c: [] for c in classes}
         for r in range(R):
-            for lst, wq in ((g_step, True), (g_gemm, False)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=cap):
+                run_set(r)
+            g_step.append(g)
+            for c in classes:
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
-                    run_set(r, wq)
-                lst.append(g)
+                    run_set(r, c)
+                g_cls[c].append(g)
         torch.cuda.synchronize()
         for r in range(R):
             g_step[r].replay()
@@ -391,96 +473,114 @@ def main():
     log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step on HIP events "
         f"({wall_ms / args.steps * 1e3:.2f} us/step wall), graphs={'on' if use_graph else 'off'}")
 
-    # ---- fused GEMM alone: average launch time over the same number of steps ----
-    if use_graph:
-        gem_ms, _ = timed(args.steps, lambda i: g_gemm[i % R].replay())
-    else:
-        gem_ms, _ = timed(args.steps, lambda i: run_set(i, False))
-    gemm_time_s = gem_ms * 1e-3 / args.steps  # per step (all pairs)
-
-    # per-(shape, M) launch times, each pair replayed in its own graph, and
-    # the same kernel on a dense-only copy (empty CSR) for the residual cost
-    per_shape = []
-    if args.per_shape and use_graph:
-        def pair_copies(p_idx):
-            # enough copies of the pair's packed layer that one pass over
-            # them is >= 512 MB, so no launch finds its weights in the
-            # 256 MB Infinity Cache
-            L = sets[0][p_idx][2]
-            n = max(2, -(-ROTATE_BYTES // L.nbytes()))
-            return [L.clone() for _ in range(n)]
-
-        def pair_time(p_idx, mode, copies):
-            # mode: "fused" (fused GEMM from codes), "dense" (same kernel,
-            # empty CSR), "unfused" (dense-only launch + the standalone
-            # residual kernel that reloads the activations and merges into
-            # y), "layer" (mq_fused_layer from fp16 X), "two" (act-quant
-            # kernel then the fused GEMM).  One graph launches every copy
-            # once; the time is per launch over several replays.
-            (sp_, M_, L0, x, qa, sa, y, ws) = sets[0][p_idx]
-            q2, s2 = torch.empty_like(qa), torch.empty_like(sa)
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                for L in copies:
-                    D = ops.PackedLayer(L.N, L.K, L.block, L.qw, L.sw, torch.zeros_like(L.row_ptr),
-                                        L.col_idx[:0], L.qr[:0], L.sr[:0])
-                    if mode == "layer":
-                        ops.fused_layer(x, L, out=y, workspace=ws)
-                    elif mode == "two":
-                        ops.quantize_act(x, q2, s2)
-                        ops.fused_gemm(q2, s2, L, out=y)
-                    else:
-                        ops.fused_gemm(qa, sa, L if mode == "fused" else D, out=y)
-                    if mode == "unfused":
-                        ops.residual_merge(qa, sa, L, y)
-            g.replay()
-            reps = max(3, -(-200 // len(copies)))
-            t_ms, _ = timed(reps, lambda i: g.replay())
-            del g
-            return t_ms * 1e-3 / (reps * len(copies))
+    # ---- each kernel's GEMM launches alone: average launch time over K steps ----
+    cls_time = {}
+    for c in classes:
+        if use_graph:
+            t_ms, _ = timed(args.steps, lambda i, c=c: g_cls[c][i % R].replay())
+        else:
+            t_ms, _ = timed(args.steps, lambda i, c=c: run_set(i, c))
+        cls_time[c] = t_ms * 1e-3 / args.steps  # seconds per step
+    # (shape, M) launch statistics: each pair's launches replayed from a graph
+    # over enough copies of its packed layer that one pass is >= 512 MB (no
+    # launch finds its weights in the 256 MB Infinity Cache); every replay is
+    # timed on its own and gives one sample of the mean launch time
+    per_pair = []
+    if use_graph and not args.no_per_pair:
+        modes = ["fused", "dense", "actq", "layer"] + (["unfused"] if args.ablation else [])
         for p_idx, (spec, M) in enumerate(pairs):
-            copies = pair_copies(p_idx)
-            t = pair_time(p_idx, "fused", copies)
-            t0 = pair_time(p_idx, "dense", copies)
-            tu = pair_time(p_idx, "unfused", copies)
-            tl = pair_time(p_idx, "layer", copies)
-            t2 = pair_time(p_idx, "two", copies)
+            (_, _, L0, x, qa, sa, y, ws, gws) = sets[0][p_idx]
+            n = max(2, -(-ROTATE_BYTES // L0.nbytes()))
+            copies = [L0.clone() for _ in range(n)]
+            q2, s2 = torch.empty_like(qa), torch.empty_like(sa)
+            res = {}
+            for mode in modes:
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    for L in copies:
+                        D = ops.PackedLayer(L.N, L.K, L.block, L.qw, L.sw, torch.zeros_like(L.row_ptr),
+                                            L.col_idx[:0], L.qr[:0], L.sr[:0])
+                        if mode == "layer":
+                            ops.fused_layer(x, L, out=y, workspace=ws)
+                        elif mode == "actq":
+                            ops.quantize_act(x, q2, s2)
+                        else:
+                            ops.fused_gemm(qa, sa, L if mode == "fused" else D, out=y, workspace=gws)
+                        if mode == "unfused":
+                            ops.residual_merge(qa, sa, L, y)
+                g.replay()
+                torch.cuda.synchronize()
+                samples = []
+                for _ in range(PAIR_REPLAYS):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    g.replay()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    samples.append(e0.elapsed_time(e1) * 1e3 / n)
+                res[mode] = samples
+                del g
             del copies
             torch.cuda.empty_cache()
+            med = {m: _pct(v, 50) for m, v in res.items()}
             gb = gemm_bytes(M, spec.N, spec.K, spec.block, spec.n_select)
-            lb = layer_bytes(M, spec.N, spec.K, spec.block, spec.n_select)
             go = gemm_ops(M, spec.N, spec.K, spec.block, spec.n_select)
-            per_shape.append(dict(K=spec.K, N=spec.N, M=M, us=round(t * 1e6, 3), dense_only_us=round(t0 * 1e6, 3),
-                                  residual_cost=round(t / t0 - 1, 4), unfused_us=round(tu * 1e6, 3),
-                                  unfused_over_fused=round(tu / t, 4), gbs=round(gb / t / 1e9, 1),
-                                  tops=round(go / t / 1e12, 2), layer_us=round(tl * 1e6, 3),
-                                  layer_one_kernel=bool(one_kernel[p_idx]),
-                                  layer_gbs=round(lb / tl / 1e9, 1), two_kernel_us=round(t2 * 1e6, 3)))
-            log(f"[bench]   K={spec.K:6d} N={spec.N:6d} M={M:5d}: gemm {t * 1e6:8.2f} us  "
-                f"{gb / t / 1e9:8.1f} GB/s ({gb / t / 1e9 / HBM_PEAK_GBS:5.1%} HBM)  "
-                f"{go / t / 1e12:8.2f} TOPS ({go / t / 1e12 / INT8_MFMA_PEAK_TOPS:5.1%} int8 MFMA)  "
-                f"dense-only {t0 * 1e6:8.2f} us (residual +{t / t0 - 1:5.1%})  "
-                f"unfused {tu * 1e6:8.2f} us (x{tu / t:5.3f})  "
-                f"layer {tl * 1e6:8.2f} us ({'one kernel' if one_kernel[p_idx] else 'two kernels'}; "
-                f"act-quant + gemm {t2 * 1e6:8.2f} us)")
+            row = dict(K=spec.K, N=spec.N, M=M, kernel=kern[p_idx], n_select=spec.n_select,
+                       us_p10=round(_pct(res["fused"], 10), 3), us_p50=round(med["fused"], 3),
+                       us_p90=round(_pct(res["fused"], 90), 3),
+                       tops=round(go / (med["fused"] * 1e-6) / 1e12, 2),
+                       dense_equiv_tops=round(2 * M * spec.N * spec.K / (med["fused"] * 1e-6) / 1e12, 2),
+                       gbs=round(gb / (med["fused"] * 1e-6) / 1e9, 1),
+                       frac_mfma=round(go / (med["fused"] * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
+                       frac_hbm=round(gb / (med["fused"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                       dense_only_us_p50=round(med["dense"], 3),
+                       residual_cost=round(med["fused"] / med["dense"] - 1, 4),
+                       act_quant_us_p50=round(med["actq"], 3),
+                       layer_us_p50=round(med["layer"], 3), layer_one_kernel=bool(one_kernel[p_idx]),
+                       samples=PAIR_REPLAYS, copies=n)
+            if "unfused" in med:
+                row["unfused_us_p50"] = round(med["unfused"], 3)
+                row["unfused_over_fused"] = round(med["unfused"] / med["fused"], 4)
+            per_pair.append(row)
+            log(f"[bench]   K={spec.K:6d} N={spec.N:6d} M={M:5d}: gemm p50 {med['fused']:9.2f} us "
+                f"(p10 {row['us_p10']:.2f}, p90 {row['us_p90']:.2f})  {row['gbs']:8.1f} GB/s "
+                f"({row['frac_hbm']:5.1%} HBM)  {row['tops']:8.1f} TOPS ({row['frac_mfma']:5.1%} int8)  "
+                f"dense-only {med['dense']:9.2f} us (residual +{row['residual_cost']:5.1%})  "
+                f"act-quant {med['actq']:7.2f} us  layer {med['layer']:9.2f} us"
+                + (f"  unfused x{row['unfused_over_fused']:.3f}" if "unfused" in med else ""))
 
-    launches = len(pairs)
-    if bound == "hbm":
-        achieved = per_step_gemm_bytes / gemm_time_s / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(achieved / HBM_PEAK_GBS, 4))
-    else:
-        achieved = per_step_ops / gemm_time_s / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_MFMA_PEAK_TOPS,
-                    unit="TOP/s", frac=round(achieved / INT8_MFMA_PEAK_TOPS, 4))
-    roof["traffic"] = traffic_from_profile(args.workload)
-    # the library runs M <= 32 on the streaming kernel, larger M on the tile kernel
-    roof["kernel"] = "gemm_stream_kernel" if max(M for _, M in pairs) <= 32 else "gemm_tile_kernel"
-    roof["launches_quantising_in_kernel"] = int(sum(one_kernel))
-    roof["avg_launch_us"] = round(gemm_time_s / launches * 1e6, 3)
-    roof["alg_bytes_per_launch"] = per_step_gemm_bytes / launches
-    roof["alg_ops_per_launch"] = per_step_ops / launches
-    if bound == "hbm" and not args.copy_calibration:
+    # ---- rooflines: each kernel's algorithmic work per launch over its
+    # average launch time; the dominant kernel (most time per step) first ----
+    def roof_of(c):
+        idx = [i for i, k in enumerate(kern) if k == c]
+        t = cls_time[c]
+        nl = len(idx)
+        if c == "gemm_stream_kernel":
+            achieved = sum(launch_bytes[i] for i in idx) / t / 1e9
+            r = dict(bound="hbm", achieved=round(achieved, 2), peak=HBM_PEAK_GBS, unit="GB/s",
+                     frac=round(achieved / HBM_PEAK_GBS, 4))
+        else:
+            achieved = sum(launch_ops[i] for i in idx) / t / 1e12
+            r = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_MFMA_PEAK_TOPS, unit="TOP/s",
+                     frac=round(achieved / INT8_MFMA_PEAK_TOPS, 4))
+        r["traffic"] = traffic_from_profile(args.workload, c)
+        r["kernel"] = c
+        r["launches_per_step"] = nl
+        r["M"] = sorted({pairs[i][1] for i in idx})
+        r["avg_launch_us"] = round(t / nl * 1e6, 3)
+        r["alg_bytes_per_launch"] = sum(launch_bytes[i] for i in idx) / nl
+        r["alg_ops_per_launch"] = sum(launch_ops[i] for i in idx) / nl
+        r["launches_quantising_in_kernel"] = int(sum(one_kernel[i] for i in idx))
+        return r
+
+    order = sorted(classes, key=lambda c: -cls_time[c])
+    roof = roof_of(order[0])
+    if len(order) > 1:
+        roof["other_kernels"] = [roof_of(c) for c in order[1:]]
+    if not args.copy_calibration:
+        roof.update(measure_mfma_ceiling(torch, ops))
+        if roof["bound"] == "mfma":
+            roof["frac_of_measured_mfma"] = round(roof["achieved"] / roof["measured_mfma_int8_tops"], 4)
         # a plain device copy measured here (outside the timed region): the
         # rate a streaming kernel reaches on this part, beside the datasheet
         # peak (not in counter runs, whose 256 MiB calibration copy must stay
@@ -497,7 +597,9 @@ def main():
         torch.cuda.synchronize()
         copy_gbs = 2 * a.numel() / (c0.elapsed_time(c1) * 1e-3 / 10) / 1e9
         roof["measured_copy_gbs"] = round(copy_gbs, 1)
-        roof["frac_of_copy"] = round(achieved / copy_gbs, 4)
+        for r in [roof] + roof.get("other_kernels", []):
+            if r["bound"] == "hbm":
+                r["frac_of_copy"] = round(r["achieved"] / copy_gbs, 4)
         del a, b
 
     if args.copy_calibration:
@@ -509,9 +611,9 @@ def main():
 
     out = {
         "metric": METRIC,
-        "value": round(per_step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
-        "unit": "GB/s",
-        "tops": round(per_step_ops / (ms_per_step * 1e-3) / 1e12, 3),
+        "value": round(per_step_ops / (ms_per_step * 1e-3) / 1e12, 3),
+        "unit": "TOP/s",
+        "gbs": round(per_step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -527,17 +629,18 @@ def main():
             "M": sorted({M for _, M in pairs}),
             "group": 128, "block": base[0][0].block, "rho": base[0][0].rho,
             "codes": "w4a4 int4 symmetric, int8 MFMA, int32 accumulators, fp32 epilogue, fp16 out",
+            "step": "mq_fused_layer (fp16 X -> fp16 Y) for every (shape, M)",
             "bytes_per_step": per_step_bytes, "ops_per_step": per_step_ops,
             "rotating_copies": R,
             "launch": "hip-graph" if use_graph else "eager",
         },
         "roofline": roof,
     }
-    if per_shape:
-        out["per_shape"] = per_shape
+    if per_pair:
+        out["per_pair"] = per_pair
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample ...")
-        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_budget)
+        out["cpu_baseline"] = cpu_baseline(layers, args.cpu_budget, host_layers)
     print(json.dumps(out), flush=True)
 
 

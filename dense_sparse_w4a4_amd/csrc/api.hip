@@ -348,7 +348,12 @@ mq_status mq_smooth_weights(const uint16_t* x_calib, int64_t T, const uint16_t* 
                             uint16_t* w_out, void* stream) {
   g_err[0] = 0;
   MQ_REQUIRE(T >= 1 && N >= 1 && K >= 1, MQ_ERR_SHAPE, "T, N and K must be >= 1");
-  MQ_REQUIRE(N * K < ((int64_t)1 << 40) && T * K < ((int64_t)1 << 40), MQ_ERR_SHAPE, "sizes too large");
+  // (row counts and K below 2^31 keep every launch's work-item count within
+  // 32 bits: the column kernels take one thread per channel and one
+  // workgroup row per 64 rows; the scaling kernel is a grid-stride loop)
+  MQ_REQUIRE(T < ((int64_t)1 << 31) && N < ((int64_t)1 << 31) && K < ((int64_t)1 << 31) &&
+                 N * K < ((int64_t)1 << 40) && T * K < ((int64_t)1 << 40),
+             MQ_ERR_SHAPE, "sizes too large");
   MQ_REQUIRE(x_calib && w && x_absmax && w_absmax && scales && w_out, MQ_ERR_NULL_PTR,
              "x_calib, w, x_absmax, w_absmax, scales and w_out must be non-NULL");
   MQ_REQUIRE((const void*)w_out != (const void*)w, MQ_ERR_ARG, "w_out must not alias w");
@@ -362,11 +367,23 @@ mq_status mq_smooth_acts(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
   g_err[0] = 0;
   MQ_REQUIRE(M >= 0 && K >= 1, MQ_ERR_SHAPE, "M must be >= 0 and K >= 1");
   MQ_REQUIRE(ldx >= K, MQ_ERR_SHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
-  MQ_REQUIRE(M * K < ((int64_t)1 << 40), MQ_ERR_SHAPE, "sizes too large");
+  MQ_REQUIRE(M < ((int64_t)1 << 31) && K < ((int64_t)1 << 31) && M * K < ((int64_t)1 << 40),
+             MQ_ERR_SHAPE, "sizes too large");
   if (M == 0) return MQ_OK;
   MQ_REQUIRE(x && scales && x_out, MQ_ERR_NULL_PTR, "x, scales and x_out must be non-NULL");
   return hip_status(launch_smooth_acts(x, M, K, ldx, scales, x_out, (hipStream_t)stream),
                     "mq_smooth_acts launch");
+}
+
+mq_status mq_measure_mfma(int32_t blocks, int32_t iters, int64_t* cycles, int32_t* sink,
+                          void* stream) {
+  g_err[0] = 0;
+  MQ_REQUIRE(blocks >= 1 && blocks <= (1 << 20) && iters >= 1 && iters <= (1 << 24), MQ_ERR_SHAPE,
+             "blocks = %d and iters = %d must be in [1, 2^20] and [1, 2^24]", blocks, iters);
+  MQ_REQUIRE(cycles && sink, MQ_ERR_NULL_PTR, "cycles and sink must be non-NULL");
+  MQ_REQUIRE(aligned16(cycles) && aligned16(sink), MQ_ERR_ALIGN, "cycles and sink must be 16-byte aligned");
+  return hip_status(launch_mfma_rate(blocks, iters, cycles, sink, (hipStream_t)stream),
+                    "mq_measure_mfma launch");
 }
 
 mq_status mq_validate_csr(const int32_t* row_ptr, const int32_t* col_idx, int64_t N, int64_t K,

@@ -154,6 +154,7 @@ hipError_t launch_smooth_weights(const uint16_t* xc, int64_t T, const uint16_t* 
                                  hipStream_t st);
 hipError_t launch_smooth_acts(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* s,
                               uint16_t* x_out, hipStream_t st);
+hipError_t launch_mfma_rate(int blocks, int iters, int64_t* cycles, int32_t* sink, hipStream_t st);
 bool tile_gemm_fits(const GemmArgs& a);
 int tile_gemm_splits(int64_t M, int64_t N, int64_t K);  // K splits the tile kernel would use
 hipError_t launch_tile_gemm(const GemmArgs& a, hipStream_t st);

@@ -42,23 +42,30 @@ __global__ __launch_bounds__(256) void scales_kernel(const float* ax, const floa
   s[k] = (x > 0.f && w > 0.f) ? sqrtf(x / w) : 1.f;
 }
 
-// out[r][c] = f16(f32(a[r][c]) * s[c])  (divide: f16(f32(a) / s[c]))
+// out[r][c] = f16(f32(a[r][c]) * s[c])  (divide: f16(f32(a) / s[c])), a
+// grid-stride loop so that any R x C fits the launch's 32-bit work-item count
 template <bool DIVIDE>
 __global__ __launch_bounds__(256) void scale_cols_kernel(const uint16_t* a, int64_t R, int64_t C,
                                                          int64_t lda, const float* s, uint16_t* out) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= R * C) return;
-  const int64_t r = i / C, c = i - r * C;
-  const float v = h2f(a[r * lda + c]);
-  // the fp32 result is materialised before the fp16 rounding: a fused
-  // mixed-precision multiply would round the exact product once, not the
-  // fp32 product, and differ at fp16 near-ties
-  float p = DIVIDE ? v / s[c] : v * s[c];
-  asm volatile("" : "+v"(p));
-  out[r * C + c] = f2h_bits(p);
+  const int64_t n = R * C;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t r = i / C, c = i - r * C;
+    const float v = h2f(a[r * lda + c]);
+    // the fp32 result is materialised before the fp16 rounding: a fused
+    // mixed-precision multiply would round the exact product once, not the
+    // fp32 product, and differ at fp16 near-ties
+    float p = DIVIDE ? v / s[c] : v * s[c];
+    asm volatile("" : "+v"(p));
+    out[r * C + c] = f2h_bits(p);
+  }
 }
 
 unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+// grid of the grid-stride kernels: at most 2^20 workgroups
+unsigned strided_blocks(int64_t n) {
+  const int64_t b = (n + 255) / 256;
+  return (unsigned)(b < ((int64_t)1 << 20) ? b : ((int64_t)1 << 20));
+}
 
 }  // namespace
 
@@ -72,14 +79,14 @@ hipError_t launch_smooth_weights(const uint16_t* xc, int64_t T, const uint16_t* 
   hipLaunchKernelGGL(colmax_kernel, dim3(blocks_for(K), (unsigned)((N + kRowsPerBlock - 1) / kRowsPerBlock)),
                      dim3(256), 0, st, w, N, K, K, aw);
   hipLaunchKernelGGL(scales_kernel, dim3(blocks_for(K)), dim3(256), 0, st, ax, aw, K, s);
-  hipLaunchKernelGGL(scale_cols_kernel<false>, dim3(blocks_for(N * K)), dim3(256), 0, st, w, N, K, K, s,
+  hipLaunchKernelGGL(scale_cols_kernel<false>, dim3(strided_blocks(N * K)), dim3(256), 0, st, w, N, K, K, s,
                      w_out);
   return hipGetLastError();
 }
 
 hipError_t launch_smooth_acts(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const float* s,
                               uint16_t* x_out, hipStream_t st) {
-  hipLaunchKernelGGL(scale_cols_kernel<true>, dim3(blocks_for(M * K)), dim3(256), 0, st, x, M, K, ldx, s,
+  hipLaunchKernelGGL(scale_cols_kernel<true>, dim3(strided_blocks(M * K)), dim3(256), 0, st, x, M, K, ldx, s,
                      x_out);
   return hipGetLastError();
 }

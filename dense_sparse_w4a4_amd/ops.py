@@ -10,7 +10,10 @@ names are aliases.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
+import inspect
 import os
 from dataclasses import dataclass
 from typing import Optional
@@ -51,6 +54,7 @@ _SIGS = {
                                          _vp, _vp, _vp, _vp, _c_i64, _vp]),
     "mq_smooth_weights": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
     "mq_smooth_acts": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp]),
+    "mq_measure_mfma": (ctypes.c_int, [_c_i32, _c_i32, _vp, _vp, _vp]),
 }
 
 _lib = None
@@ -101,6 +105,21 @@ def _stream(stream=None):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _on_stream(fn):
+    """Run the wrapped entry point with its `stream` argument (when one is
+    given) as the current stream, so the outputs and workspaces it allocates
+    belong to that stream: the caching allocator then never hands their
+    memory to other work while the call's kernels may still use it."""
+    sig = inspect.signature(fn)
+
+    @functools.wraps(fn)
+    def wrapper(*args, **kwargs):
+        stream = sig.bind(*args, **kwargs).arguments.get("stream")
+        with torch.cuda.stream(stream) if stream is not None else contextlib.nullcontext():
+            return fn(*args, **kwargs)
+    return wrapper
+
+
 def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
@@ -113,6 +132,7 @@ def _dev(t: torch.Tensor, dtype, name: str) -> torch.Tensor:
 # Entry points
 # ----------------------------------------------------------------------------
 
+@_on_stream
 def quantize_act(x: torch.Tensor, qa: Optional[torch.Tensor] = None,
                  sa: Optional[torch.Tensor] = None, stream=None):
     """x fp16 [M, K] (row stride % 8 == 0) -> (qa uint8 [M, K/2], sa fp32 [M, K/128])."""
@@ -129,6 +149,7 @@ def quantize_act(x: torch.Tensor, qa: Optional[torch.Tensor] = None,
     return qa, sa
 
 
+@_on_stream
 def select_blocks(w: torch.Tensor, x_calib: torch.Tensor, block: int, n_select: int,
                   stream=None):
     """Delta-score top-K.  Returns (selected int32 [n_select] ascending,
@@ -178,6 +199,7 @@ class PackedLayer:
                            self.sr.clone())
 
 
+@_on_stream
 def pack_weights(w: torch.Tensor, block: int, selected: torch.Tensor, stream=None) -> PackedLayer:
     """w fp16 [N, K] + ascending selected block ids -> PackedLayer."""
     _dev(w, torch.float16, "w")
@@ -207,6 +229,7 @@ def fused_gemm_workspace(M: int, N: int, K: int) -> int:
     return int(n.value)
 
 
+@_on_stream
 def fused_gemm(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer,
                out: Optional[torch.Tensor] = None, dump: bool = False,
                workspace: Optional[torch.Tensor] = None, stream=None):
@@ -251,6 +274,7 @@ def fused_layer_workspace(M: int, N: int, K: int) -> int:
     return int(n.value)
 
 
+@_on_stream
 def fused_layer(x: torch.Tensor, layer: PackedLayer, out: Optional[torch.Tensor] = None,
                 workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     """Y fp16 [M, N] from fp16 activations: Qa(X) and the fused GEMM, as one
@@ -280,6 +304,7 @@ def fused_layer(x: torch.Tensor, layer: PackedLayer, out: Optional[torch.Tensor]
     return out
 
 
+@_on_stream
 def residual_merge(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer, out: torch.Tensor,
                    stream=None) -> torch.Tensor:
     """Unfused ablation: out += deq(Qa(X) R^T) by a standalone residual kernel."""
@@ -297,6 +322,7 @@ def residual_merge(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer, out: 
     return out
 
 
+@_on_stream
 def smooth_weights(x_calib: torch.Tensor, w: torch.Tensor, stream=None):
     """Outlier migration: -> (scales fp32 [K], migrated w fp16 [N, K], x_absmax, w_absmax)."""
     _dev(x_calib, torch.float16, "x_calib")
@@ -314,6 +340,7 @@ def smooth_weights(x_calib: torch.Tensor, w: torch.Tensor, stream=None):
     return s, w_out, ax, aw
 
 
+@_on_stream
 def smooth_acts(x: torch.Tensor, scales: torch.Tensor, stream=None) -> torch.Tensor:
     """Migrated activations x / scales (fp16 [M, K])."""
     _dev(x, torch.float16, "x")
@@ -334,6 +361,19 @@ def validate_csr(layer: PackedLayer, stream=None) -> None:
         layer.block, ns, _stream(stream)))
 
 
+@_on_stream
+def measure_mfma(blocks: int, iters: int, stream=None):
+    """Launch the matrix-core rate probe (measurement only).  Returns the
+    device tensors (cycles int64 [4*blocks], sink int32 [256*blocks]); the
+    caller times the launch."""
+    dev = torch.device("cuda", torch.cuda.current_device())
+    cycles = torch.empty(4 * blocks, dtype=torch.int64, device=dev)
+    sink = torch.empty(256 * blocks, dtype=torch.int32, device=dev)
+    _check("mq_measure_mfma", lib().mq_measure_mfma(blocks, iters, _ptr(cycles), _ptr(sink),
+                                                    _stream(stream)))
+    return cycles, sink
+
+
 def layer_forward(x: torch.Tensor, layer: PackedLayer, out: Optional[torch.Tensor] = None,
                   stream=None) -> torch.Tensor:
     """The online hot path: Qa(X) then the fused GEMM (two launches)."""
@@ -352,3 +392,4 @@ mq_validate_csr = validate_csr
 mq_residual_merge = residual_merge
 mq_smooth_weights = smooth_weights
 mq_smooth_acts = smooth_acts
+mq_measure_mfma = measure_mfma

@@ -262,7 +262,8 @@ mq_status mq_residual_merge(const uint8_t* qa, const float* sa, int64_t M, int64
  *   x_calib : fp16 [T][K];  w : fp16 [N][K]
  *   x_absmax, w_absmax, scales : fp32 [K] (outputs)
  *   w_out   : fp16 [N][K] (output; must not alias w)
- *   T, N >= 1, K >= 1.
+ *   1 <= T, N, K < 2^31 and N*K, T*K < 2^40 (else MQ_ERR_SHAPE, nothing
+ *   enqueued).
  */
 mq_status mq_smooth_weights(const uint16_t* x_calib, int64_t T, const uint16_t* w, int64_t N,
                             int64_t K, float* x_absmax, float* w_absmax, float* scales,
@@ -272,9 +273,26 @@ mq_status mq_smooth_weights(const uint16_t* x_calib, int64_t T, const uint16_t* 
  * Migrated activations: x_out[m][k] = f16(x[m][k] / scales[k]).
  *   x : fp16 [M][ldx] (ldx >= K);  scales : fp32 [K] from mq_smooth_weights
  *   x_out : fp16 [M][K] (output).  M == 0 enqueues nothing.
+ *   0 <= M < 2^31, 1 <= K < 2^31, M*K < 2^40 (else MQ_ERR_SHAPE).
  */
 mq_status mq_smooth_acts(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                          const float* scales, uint16_t* x_out, void* stream);
+
+/*
+ * Measurement only (not part of the layer): the sustained rate of the int8
+ * matrix-core instruction the fused GEMM kernels use
+ * (V_MFMA_I32_16X16X64_I8) and the shader clock, as the roofline
+ * denominators measured on the device.  Launches `blocks` workgroups of four
+ * waves; each wave runs `iters` rounds of four independent MFMA chains and
+ * stores its shader-cycle count (s_memtime delta) in cycles[4*block + wave].
+ * Each round is 4 x 2*16*16*64 = 131072 integer ops per wave.  The caller
+ * times the launch (e.g. with HIP events) and derives ops/s and cycles/s.
+ *   blocks in [1, 2^20], iters in [1, 2^24]
+ *   cycles : int64 [4*blocks] (output)
+ *   sink   : int32 [256*blocks] (output; keeps the results live)
+ */
+mq_status mq_measure_mfma(int32_t blocks, int32_t iters, int64_t* cycles, int32_t* sink,
+                          void* stream);
 
 /*
  * Synchronous CSR check (copies row_ptr and col_idx to the host and waits

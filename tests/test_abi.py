@@ -171,3 +171,28 @@ def test_fused_layer_workspace_and_validation(L):
     assert _layer_call(L, M=16) == WS                     # two-kernel route needs the workspace
     assert _layer_call(L, M=16, ws=P, wsb=16 * 256 + 16 * 4 * 4 - 1) == WS
     assert _layer_call(L, M=0, x=None, y=None) == OK      # empty batch
+
+
+def test_smooth_size_limits(L):
+    # sizes whose launches would exceed 32-bit work-item counts are refused
+    # before anything is enqueued (fake pointers are never dereferenced)
+    big = 1 << 31
+    fw = L.mq_smooth_weights
+    assert fw(P, 4, P, 4, 0, P, P, P, ctypes.c_void_p(0x2000), None) == SHAPE       # K < 1
+    assert fw(P, big, P, 4, 1, P, P, P, ctypes.c_void_p(0x2000), None) == SHAPE     # T >= 2^31
+    assert fw(P, 4, P, big, 1, P, P, P, ctypes.c_void_p(0x2000), None) == SHAPE     # N >= 2^31
+    assert fw(P, 4, P, 1 << 21, 1 << 19, P, P, P, ctypes.c_void_p(0x2000), None) == SHAPE  # N*K = 2^40
+    assert fw(P, 4, P, 4, 8, P, P, P, P, None) == ARG                               # w_out aliases w
+    fa = L.mq_smooth_acts
+    assert fa(P, big, 8, 8, P, P, None) == SHAPE                                    # M >= 2^31
+    assert fa(P, 4, big, big, P, P, None) == SHAPE                                  # K >= 2^31
+    assert fa(P, 1 << 21, 1 << 19, 1 << 19, P, P, None) == SHAPE                    # M*K = 2^40
+    assert fa(None, 0, 8, 8, None, None, None) == OK                                # empty batch
+
+
+def test_measure_mfma_validation(L):
+    f = L.mq_measure_mfma
+    assert f(0, 10, P, P, None) == SHAPE
+    assert f(4, 0, P, P, None) == SHAPE
+    assert f(4, 10, None, P, None) == NULLP
+    assert f(4, 10, P, PMIS, None) == ALIGN

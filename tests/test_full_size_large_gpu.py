@@ -76,7 +76,17 @@ def _check(spec, Ms):
 
 @pytest.mark.parametrize("K,N", syn.QWEN3_32B_SHAPES)
 def test_full_size_qwen3_32b(K, N):
-    _check(syn.qwen3_32b(K, N), [1, 16, 4096])
+    # every M of the Qwen3-32B sweep; at M = 256, K = 25600 the tile kernel
+    # splits the 200 groups over 6 workgroups (33 or 34 groups each)
+    _check(syn.qwen3_32b(K, N), syn.QWEN3_32B_M)
+
+
+@pytest.mark.parametrize("K,N", syn.LLAMA3_8B_SHAPES)
+def test_full_size_llama3_8b_decode(K, N):
+    # the decode launches the benchmark's secondary workload times (M = 1
+    # and 4 as one kernel quantising in its prologue where the shape allows,
+    # M = 16 through act-quant + fused GEMM)
+    _check(syn.llama3_8b(K, N), syn.LLAMA3_8B_DECODE_M)
 
 
 @pytest.mark.parametrize("b,rho", [(32, 0.20), (64, 0.10), (128, 0.05)])

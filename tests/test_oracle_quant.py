@@ -171,3 +171,26 @@ def test_pack_roundtrip(shape):
     p = oracle.pack_nibbles(q)
     assert p.shape == shape[:-1] + (shape[-1] // 2,)
     assert np.array_equal(oracle.unpack_nibbles(p), q)
+
+
+def test_golden_residual_row():
+    # one block row of the residual, derived by hand (see the fixture): the
+    # base error, the fp16 row scale bits, the residual codes and bytes
+    f = json.load(open(GOLD))["residual_row_b32"]
+    b = f["block"]
+    w = np.zeros((b, 128), np.float16)
+    w[0, :len(f["values"])] = f["values"]
+    qw, sw = oracle.quantize_base(w)
+    n = len(f["values"])
+    assert qw[0, :n].tolist() == f["base_codes"] and float(sw[0, 0]) == 1.0
+    E = oracle.base_error(w, qw, sw)
+    assert E[0, :n].tolist() == f["errors"]
+    qr, sr, rhat = oracle.residual_all_blocks(E, b)
+    assert int(sr.view(np.uint16)[0, 0, 0]) == f["sr_f16_bits"]
+    assert float(sr[0, 0, 0]) == f["sr"]
+    assert qr[0, :n].tolist() == f["codes"] and not np.any(qr[0, n:b])
+    assert rhat[0, :n].tolist() == f["rhat"]
+    packed = oracle.pack_weights(w, b, np.array([0]))
+    assert packed["qr"][0, 0, :3].tolist() == f["qr_bytes"]
+    assert not np.any(packed["qr"][0, 0, 3:]) and not np.any(packed["qr"][0, 1:])
+    assert int(packed["sr"].view(np.uint16)[0, 0]) == f["sr_f16_bits"]

@@ -100,6 +100,24 @@ def test_select_ties_and_extremes():
     assert host(sel).tolist() == list(range(spec.n_blocks))
 
 
+def test_pack_golden_residual_row():
+    # the hand-derived residual row (tests/golden/hand_quant.json): the GPU's
+    # packed bytes and scale bits against the stored values directly
+    import json
+    import os
+    f = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "hand_quant.json")))["residual_row_b32"]
+    b = f["block"]
+    w = np.zeros((b, 128), np.float16)
+    w[0, :len(f["values"])] = f["values"]
+    layer = ops.pack_weights(dev(w), b, torch.zeros(1, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    qr, sr = host(layer.qr), host(layer.sr).view(np.uint16)
+    assert qr[0, 0, :3].tolist() == f["qr_bytes"]
+    assert not np.any(qr[0, 0, 3:]) and not np.any(qr[0, 1:])
+    assert int(sr[0, 0]) == f["sr_f16_bits"] and not np.any(sr[0, 1:])
+    assert host(layer.row_ptr).tolist() == [0, 1] and host(layer.col_idx).tolist() == [0]
+
+
 @pytest.mark.parametrize("b,rho", [(32, 0.1), (64, 0.0), (64, 0.1), (64, 1.0), (128, 0.2)])
 def test_pack_bit_exact(b, rho):
     spec = syn.TINY.with_block(b, rho)
@@ -132,6 +150,9 @@ GEMM_CASES = [
     (300, 256, 2048, 64, 0.10),
     (40, 128, 4096, 128, 0.25),
     (129, 384, 3072, 32, 0.15),
+    # uneven split-K: 25 groups over 3 splits of 8, 8 and 9 groups (an odd
+    # count in the last split)
+    (40, 128, 3200, 64, 0.10),
 ]
 
 
@@ -218,7 +239,8 @@ def test_full_size_llama3_8b(K, N, M):
     tiles = sorted({0, NT - 1, int(np.argmax(counts)), NT // 2})
     yt = host(y)
     for nt, yref in tile_rows_reference(rqa, rsa, ref, tiles).items():
-        assert_y_close(torch.from_numpy(yt[:, nt * 64:(nt + 1) * 64]), yref)
+        b = spec.block
+        assert_y_close(torch.from_numpy(yt[:, nt * b:(nt + 1) * b]), yref)
 
 
 def test_graph_replay_matches_eager():
