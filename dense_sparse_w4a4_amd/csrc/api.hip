@@ -4,6 +4,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <vector>
 
 #include "mq_internal.h"
@@ -230,12 +231,20 @@ mq_status mq_fused_layer_workspace(int64_t M, int64_t N, int64_t K, size_t* byte
   return MQ_OK;
 }
 
-mq_status mq_fused_layer(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int64_t N,
-                         const uint8_t* qw, const uint16_t* sw, int32_t block, int32_t n_select,
-                         const int32_t* row_ptr, const int32_t* col_idx, const uint8_t* qr,
-                         const uint16_t* sr, uint16_t* y, int64_t ldy, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace mq {
+
+// Argument checks of the one-call layer (mq_fused_layer and its
+// allocation-free variant).  *empty is set for M == 0 (nothing to enqueue);
+// *need is the workspace the shape uses.
+static mq_status layer_check(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int64_t N,
+                             const uint8_t* qw, const uint16_t* sw, int32_t block, int32_t n_select,
+                             const int32_t* row_ptr, const int32_t* col_idx, const uint8_t* qr,
+                             const uint16_t* sr, uint16_t* y, int64_t ldy, const void* workspace,
+                             bool* empty, size_t* need) {
+  *empty = false;
+  *need = 0;
   MQ_REQUIRE(valid_block(block), MQ_ERR_BLOCK, "block = %d must be 32, 64 or 128", block);
   MQ_REQUIRE(M >= 0, MQ_ERR_SHAPE, "M = %lld must be >= 0", (long long)M);
   MQ_REQUIRE(N > 0 && N % block == 0, MQ_ERR_SHAPE, "N = %lld must be a positive multiple of %d",
@@ -252,7 +261,10 @@ mq_status mq_fused_layer(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, i
              "packed weights and activations must each be below 4 GiB");
   MQ_REQUIRE(n_select >= 0 && n_select <= B, MQ_ERR_BUDGET, "n_select = %d outside [0, %lld]",
              n_select, (long long)B);
-  if (M == 0) return MQ_OK;
+  if (M == 0) {
+    *empty = true;
+    return MQ_OK;
+  }
   MQ_REQUIRE(x && qw && sw && y, MQ_ERR_NULL_PTR, "x, qw, sw and y must be non-NULL");
   MQ_REQUIRE(n_select == 0 || (row_ptr && col_idx && qr && sr), MQ_ERR_NULL_PTR,
              "row_ptr, col_idx, qr and sr must be non-NULL when n_select > 0");
@@ -262,9 +274,19 @@ mq_status mq_fused_layer(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, i
                  aligned16(row_ptr) && aligned16(col_idx) && aligned16(qr) && aligned16(sr) &&
                  aligned16(workspace),
              MQ_ERR_ALIGN, "device pointers must be 16-byte aligned");
-  const size_t need = layer_workspace(M, N, K);
-  MQ_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), MQ_ERR_WORKSPACE,
-             "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  *need = layer_workspace(M, N, K);
+  return MQ_OK;
+}
+
+// Launches of the one-call layer on `ws` (at least layer_workspace's bytes;
+// unused when that is 0): one kernel when the streaming GEMM quantises the
+// activations itself, else act-quant into the workspace, then the fused
+// GEMM with its split-K partials after the codes and scales.
+static mq_status layer_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int64_t N,
+                           const uint8_t* qw, const uint16_t* sw, int32_t block, int32_t n_select,
+                           const int32_t* row_ptr, const int32_t* col_idx, const uint8_t* qr,
+                           const uint16_t* sr, uint16_t* y, int64_t ldy, uint8_t* ws, size_t need,
+                           hipStream_t st) {
   GemmArgs a = {};
   a.M = M;
   a.N = N;
@@ -283,14 +305,13 @@ mq_status mq_fused_layer(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, i
   if (need == 0) {  // one kernel: the streaming GEMM quantises the activations itself
     a.x = x;
     a.ldx = ldx;
-    return hip_status(launch_fused_gemm(a, (hipStream_t)stream), "mq_fused_layer launch");
+    return hip_status(launch_fused_gemm(a, st), "mq_fused_layer launch");
   }
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* qa = ws;
   float* sa = reinterpret_cast<float*>(ws + round256((size_t)M * (size_t)(K / 2)));
-  const mq_status st = hip_status(launch_act_quant(x, M, K, ldx, qa, sa, (hipStream_t)stream),
-                                  "mq_fused_layer act-quant launch");
-  if (st != MQ_OK) return st;
+  const mq_status s = hip_status(launch_act_quant(x, M, K, ldx, qa, sa, st),
+                                 "mq_fused_layer act-quant launch");
+  if (s != MQ_OK) return s;
   a.qa = qa;
   a.sa = sa;
   const size_t split = split_workspace(M, N, K);
@@ -298,7 +319,80 @@ mq_status mq_fused_layer(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, i
     a.part = reinterpret_cast<float*>(ws + need - split);
     a.ksplit = tile_gemm_splits(M, N, K);
   }
-  return hip_status(launch_fused_gemm(a, (hipStream_t)stream), "mq_fused_layer launch");
+  return hip_status(launch_fused_gemm(a, st), "mq_fused_layer launch");
+}
+
+// Device scratch of mq_fused_layer_noalloc (each device holds its own copy
+// of this array from the time the library's code object is loaded on it
+// until the process ends).  In host code `scratch` only names the symbol:
+// the address a kernel may use is the one hipGetSymbolAddress returns for
+// the current device, looked up once per device and kept in g_scratch.
+constexpr size_t kScratchBytes = MQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch[kMaxDevices];
+
+static mq_status scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "mq_fused_layer_noalloc hipGetDevice");
+  MQ_REQUIRE(dev >= 0 && dev < kMaxDevices, MQ_ERR_HIP, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "mq_fused_layer_noalloc hipGetSymbolAddress");
+    MQ_REQUIRE(p != nullptr, MQ_ERR_HIP, "scratch has no device address");
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return MQ_OK;
+}
+
+}  // namespace mq
+
+extern "C" {
+
+mq_status mq_fused_layer(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int64_t N,
+                         const uint8_t* qw, const uint16_t* sw, int32_t block, int32_t n_select,
+                         const int32_t* row_ptr, const int32_t* col_idx, const uint8_t* qr,
+                         const uint16_t* sr, uint16_t* y, int64_t ldy, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  bool empty = false;
+  size_t need = 0;
+  mq_status s = layer_check(x, M, K, ldx, N, qw, sw, block, n_select, row_ptr, col_idx, qr, sr, y,
+                            ldy, workspace, &empty, &need);
+  if (s != MQ_OK || empty) return s;
+  MQ_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), MQ_ERR_WORKSPACE,
+             "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  return layer_run(x, M, K, ldx, N, qw, sw, block, n_select, row_ptr, col_idx, qr, sr, y, ldy,
+                   static_cast<uint8_t*>(workspace), need, (hipStream_t)stream);
+}
+
+mq_status mq_fused_layer_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int64_t N,
+                                 const uint8_t* qw, const uint16_t* sw, int32_t block,
+                                 int32_t n_select, const int32_t* row_ptr, const int32_t* col_idx,
+                                 const uint8_t* qr, const uint16_t* sr, uint16_t* y, int64_t ldy,
+                                 void* stream) {
+  g_err[0] = 0;
+  bool empty = false;
+  size_t need = 0;
+  mq_status s = layer_check(x, M, K, ldx, N, qw, sw, block, n_select, row_ptr, col_idx, qr, sr, y,
+                            ldy, nullptr, &empty, &need);
+  if (s != MQ_OK || empty) return s;
+  MQ_REQUIRE(need <= kScratchBytes, MQ_ERR_WORKSPACE,
+             "this shape needs %zu bytes of scratch; the allocation-free entry point has %zu "
+             "(use mq_fused_layer with a workspace)", need, kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    s = scratch_address(&ws);
+    if (s != MQ_OK) return s;
+  }
+  return layer_run(x, M, K, ldx, N, qw, sw, block, n_select, row_ptr, col_idx, qr, sr, y, ldy,
+                   static_cast<uint8_t*>(ws), need, (hipStream_t)stream);
 }
 
 mq_status mq_residual_merge(const uint8_t* qa, const float* sa, int64_t M, int64_t N, int64_t K,

@@ -55,7 +55,11 @@ _SIGS = {
     "mq_smooth_weights": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
     "mq_smooth_acts": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp]),
     "mq_measure_mfma": (ctypes.c_int, [_c_i32, _c_i32, _vp, _vp, _vp]),
+    "mq_fused_layer_noalloc": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i32,
+                                              _c_i32, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
 }
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -304,6 +308,29 @@ def fused_layer(x: torch.Tensor, layer: PackedLayer, out: Optional[torch.Tensor]
     return out
 
 
+def fused_layer_noalloc(x: torch.Tensor, layer: PackedLayer, out: torch.Tensor,
+                        stream=None) -> torch.Tensor:
+    """fused_layer without a workspace: the library's per-device scratch
+    serves instead (same y bits).  Allocates nothing; `out` is required.
+    Calls that overlap on one device race on the scratch."""
+    _dev(x, torch.float16, "x")
+    _dev(out, torch.float16, "out")
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise ValueError("x must be [M, K] with unit column stride")
+    M, K = x.shape
+    N, b, ns = layer.N, layer.block, layer.n_select
+    if K != layer.K:
+        raise ValueError("x must match the layer's K")
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != M or out.shape[1] != N:
+        raise ValueError("out must be [M, N] with unit column stride")
+    _check("mq_fused_layer_noalloc", lib().mq_fused_layer_noalloc(
+        _ptr(x), M, K, x.stride(0), N, _ptr(layer.qw), _ptr(layer.sw), b, ns,
+        _ptr(layer.row_ptr) if ns else None, _ptr(layer.col_idx) if ns else None,
+        _ptr(layer.qr) if ns else None, _ptr(layer.sr) if ns else None,
+        _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
 @_on_stream
 def residual_merge(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer, out: torch.Tensor,
                    stream=None) -> torch.Tensor:
@@ -388,6 +415,7 @@ mq_fused_gemm = fused_gemm
 mq_fused_gemm_workspace = fused_gemm_workspace
 mq_fused_layer = fused_layer
 mq_fused_layer_workspace = fused_layer_workspace
+mq_fused_layer_noalloc = fused_layer_noalloc
 mq_validate_csr = validate_csr
 mq_residual_merge = residual_merge
 mq_smooth_weights = smooth_weights

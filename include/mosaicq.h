@@ -232,6 +232,32 @@ mq_status mq_fused_layer(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, i
                          uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                          void* stream);
 
+/* Device scratch of mq_fused_layer_noalloc, per device: 64 MiB. */
+#define MQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+/*
+ * mq_fused_layer for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same launches and the same y bits as mq_fused_layer, with the
+ * workspace (activation codes and scales, split-K partials) taken from a
+ * device scratch array of MQ_NOALLOC_SCRATCH_BYTES that the library holds on
+ * each device from the time its code is loaded there until the process
+ * ends.  The call allocates nothing.  Every size with
+ * mq_fused_layer_workspace(M, N, K) <= MQ_NOALLOC_SCRATCH_BYTES is accepted
+ * (every configured shape up to M = 4096, K = 25600); larger ones return
+ * MQ_ERR_WORKSPACE with nothing enqueued.  The first call on a device looks
+ * up that device's scratch address (thread-safe).
+ * Calls whose launches overlap on one device race on the scratch (for
+ * example two streams of one device): the caller serialises them.  Nothing
+ * in the scratch needs to start at zero.
+ *   Arguments as for mq_fused_layer, without the workspace.
+ */
+mq_status mq_fused_layer_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int64_t N,
+                                 const uint8_t* qw, const uint16_t* sw, int32_t block,
+                                 int32_t n_select, const int32_t* row_ptr, const int32_t* col_idx,
+                                 const uint8_t* qr, const uint16_t* sr, uint16_t* y, int64_t ldy,
+                                 void* stream);
+
 /*
  * Unfused ablation (measurement only; the layer's path never needs it): the
  * residual branch as a standalone kernel.  It reloads the activation codes,

@@ -196,3 +196,24 @@ def test_measure_mfma_validation(L):
     assert f(4, 0, P, P, None) == SHAPE
     assert f(4, 10, None, P, None) == NULLP
     assert f(4, 10, P, PMIS, None) == ALIGN
+
+
+def test_fused_layer_noalloc_validation(L):
+    f = L.mq_fused_layer_noalloc
+
+    def call(**kw):
+        a = dict(x=P, M=4, K=512, ldx=512, N=512, qw=P, sw=P, b=64, ns=6, rp=P, ci=P, qr=P, sr=P,
+                 y=P, ldy=512)
+        a.update(kw)
+        return f(a["x"], a["M"], a["K"], a["ldx"], a["N"], a["qw"], a["sw"], a["b"], a["ns"], a["rp"],
+                 a["ci"], a["qr"], a["sr"], a["y"], a["ldy"], None)
+    assert call(b=100) == BLOCK
+    assert call(K=500) == SHAPE
+    assert call(ns=65) == BUDGET
+    assert call(x=None) == NULLP
+    assert call(x=PMIS) == ALIGN
+    assert call(M=0, x=None, y=None) == OK
+    # a shape whose workspace passes the 64 MiB scratch is refused before any
+    # device call
+    assert call(M=8192, K=25600, ldx=25600, N=128, ldy=128, ns=0) == WS
+    assert "scratch" in ops.last_error()
