@@ -39,10 +39,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   // amax >= |value| (checked exhaustively on the host), at three operations
   // per code instead of a division
   const float r = s == 0.0f ? 0.0f : 1.0f / s;
-  int q[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) q[i] = quant4_rcp(f[i], s, r);
-  *reinterpret_cast<uint32_t*>(qa + m * (K / 2) + j * (kGroup / 2) + t * 4) = pack8(q);
+  *reinterpret_cast<uint32_t*>(qa + m * (K / 2) + j * (kGroup / 2) + t * 4) = quant4_word(f, s, r);
   if (t == 0) sa[m * G + j] = s;
 }
 

@@ -308,10 +308,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
       amax = row16_max(amax);
       const float sc = amax / 7.0f;
       const float r = sc == 0.0f ? 0.0f : 1.0f / sc;
-      int q[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) q[i] = quant4_rcp(f[i], sc, r);
-      *reinterpret_cast<uint32_t*>(qa_t + row * qrow + j * 64 + tl * 4) = pack8(q);
+      *reinterpret_cast<uint32_t*>(qa_t + row * qrow + j * 64 + tl * 4) = quant4_word(f, sc, r);
       if (tl == 0) sa_t[j * 16 + row] = sc * kInv256;
     }
   }

@@ -28,10 +28,12 @@ __device__ __forceinline__ uint16_t f2h_bits(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
-// Symmetric 4-bit code: clamp(rint(v / s), -7, 7), 0 when s == 0.
+// Symmetric 4-bit code: clamp(rint(v / s), -7, 7), 0 when s == 0 or when
+// the quotient is not a number (inf/inf).
 __device__ __forceinline__ int quant4(float v, float s) {
   if (s == 0.0f) return 0;
   float r = rintf(v / s);
+  if (r != r) return 0;
   r = fminf(fmaxf(r, -7.0f), 7.0f);
   return (int)r;
 }
@@ -39,10 +41,12 @@ __device__ __forceinline__ int quant4(float v, float s) {
 // The same code from the reciprocal r = 1/s (r = 0 when s = 0): q0 = v*r,
 // e = v - q0*s (one fma, exact), q1 = q0 + e*r (one fma), which is the
 // correctly rounded quotient v/s (Markstein's correction).  An exhaustive
-// check over every fp16 v and every scale s = amax/7 with fp16 amax >= |v|
-// finds q1 equal to the IEEE quotient except for the sign of a zero
-// quotient, so the codes equal quant4's; three operations per code instead
-// of a full division.
+// check over every finite fp16 amax, every scale s = amax/7 and every fp16
+// v with |v| <= amax finds q1 equal to the IEEE quotient except for the
+// sign of a zero quotient, so the codes equal quant4's; three operations
+// per code instead of a full division.  For an infinite scale (a group
+// holding +-inf) the caller replaces the group's codes by quant4's, all 0
+// (see quant4_word).
 __device__ __forceinline__ int quant4_rcp(float v, float s, float r) {
   const float q0 = v * r;
   const float e = fmaf(-q0, s, v);
@@ -68,6 +72,16 @@ __device__ __forceinline__ uint32_t pack8(const int q[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) w |= ((uint32_t)q[i] & 0xFu) << (4 * i);
   return w;
+}
+
+// Eight codes of one activation group under scale s (reciprocal r), packed:
+// the reciprocal route for a finite scale; for s = +inf (the group holds an
+// infinite value) every code is quant4's, 0 (v/inf = 0, inf/inf -> 0).
+__device__ __forceinline__ uint32_t quant4_word(const float f[8], float s, float r) {
+  int q[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) q[i] = quant4_rcp(f[i], s, r);
+  return s < __builtin_inff() ? pack8(q) : 0u;
 }
 
 // Eight fp16 values held in a uint4 -> floats.

@@ -34,7 +34,11 @@
  *     synchronisation.  No call aborts or throws.
  *   - Device pointers must be 16-byte aligned; leading dimensions are in
  *     elements.
- *   - Inputs must be finite; NaN or Inf inputs give unspecified codes.
+ *   - Weights must be finite.  Activations may hold +-inf: a group whose
+ *     largest magnitude is infinite gets scale +inf and codes 0 (the IEEE
+ *     quotient v/inf is 0; inf/inf, not a number, gives 0 too), so y is
+ *     NaN wherever that group contributes.  NaN inputs give unspecified
+ *     codes.
  */
 #ifndef MOSAICQ_H
 #define MOSAICQ_H

@@ -37,14 +37,16 @@ def quant4(v: np.ndarray, s: np.ndarray) -> np.ndarray:
 
     [summary-pt] Metodologia 1: both the base and the residual are 4-bit.
     Reading: symmetric range [-7, 7], the quotient formed by an IEEE fp32
-    division and rounded half-to-even.
+    division and rounded half-to-even.  A quotient that is not a number
+    (inf/inf in a group whose largest magnitude is infinite) gives code 0,
+    as the finite values of such a group do (v/inf = 0).
     """
     v32 = np.asarray(v, dtype=np.float32)
     s32 = np.asarray(s, dtype=np.float32)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         r = np.rint(v32 / s32)
     q = np.clip(r, -QMAX, QMAX)
-    q = np.where(s32 == 0, np.float32(0), q)
+    q = np.where((s32 == 0) | np.isnan(q), np.float32(0), q)
     return q.astype(np.int8)
 
 

@@ -74,13 +74,15 @@ def test_fused_layer_matches_two_kernels_and_oracle(M, N, K, b, rho, one_kernel)
 
 
 def test_fused_layer_special_values_and_padded_rows():
-    # all-zero groups, subnormals, fp16 extremes, exact .5 ties of v/s, and a
-    # leading dimension larger than K
+    # all-zero groups, an infinite value (its group's codes are 0 and y is NaN
+    # on that row on both routes), subnormals, fp16 extremes, exact .5 ties
+    # of v/s, and a leading dimension larger than K
     K, N, b = 512, 256, 64
     spec = syn.LayerSpec("s", K=K, N=N, T=32, block=b, rho=0.2)
     w, xc, layer = _gpu_layer(spec, seed=3)
     rng = np.random.default_rng(5)
     x = np.zeros((4, K), np.float16)
+    x[0, 300] = np.inf                                   # group 2 of row 0: scale +inf, codes 0
     x[1, :] = (rng.standard_normal(K) * 1e-6).astype(np.float16)
     x[2, :] = np.float16(65504.0) * np.sign(rng.standard_normal(K)).astype(np.float16)
     x[3, :128] = np.arange(128) * 0.5 - 32
@@ -98,6 +100,7 @@ def test_fused_layer_special_values_and_padded_rows():
         assert np.array_equal(_bits(y), _bits(y2)), f"M={M}"
         rqa, rsa = oracle.quantize_act(x[:M])
         assert np.array_equal(host(qa), oracle.pack_nibbles(rqa))
+        assert np.array_equal(host(sa).view(np.uint32), rsa.view(np.uint32))
 
 
 @pytest.mark.parametrize("K,N", syn.LLAMA3_8B_SHAPES)

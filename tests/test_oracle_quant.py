@@ -194,3 +194,17 @@ def test_golden_residual_row():
     assert packed["qr"][0, 0, :3].tolist() == f["qr_bytes"]
     assert not np.any(packed["qr"][0, 0, 3:]) and not np.any(packed["qr"][0, 1:])
     assert int(packed["sr"].view(np.uint16)[0, 0]) == f["sr_f16_bits"]
+
+
+def test_infinite_group_rule():
+    # a group whose largest magnitude is infinite: scale +inf and every code 0
+    # (v/inf = 0 for finite v; inf/inf is not a number and gives 0 too)
+    x = np.ones((2, 256), np.float16)
+    x[0, 5] = np.inf
+    x[1, 130] = -np.inf
+    x[1, 131] = np.inf
+    qa, sa = oracle.quantize_act(x)
+    assert np.isposinf(sa[0, 0]) and np.isposinf(sa[1, 1])
+    assert not np.any(qa[0, :128]) and not np.any(qa[1, 128:])
+    assert np.all(qa[0, 128:] == 7) and np.all(qa[1, :128] == 7)
+    assert oracle.quant4(np.array([np.inf, -np.inf, 3.0], np.float32), np.float32(np.inf)).tolist() == [0, 0, 0]

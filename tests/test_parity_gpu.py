@@ -54,7 +54,7 @@ def test_act_quant_bit_exact(M, K, pad):
 
 def test_act_quant_special_values():
     rng = np.random.default_rng(0)
-    x = np.zeros((6, 256), np.float16)
+    x = np.zeros((8, 256), np.float16)
     x[0, :] = 0                                                    # all-zero groups
     x[1, :] = (rng.standard_normal(256) * 1e-6).astype(np.float16)  # subnormals
     x[2, :] = np.float16(65504.0) * np.sign(rng.standard_normal(256)).astype(np.float16)
@@ -62,6 +62,10 @@ def test_act_quant_special_values():
     x[4, :128] = 7.0 * (np.arange(128) % 3 - 1)
     x[4, 128:] = np.linspace(-3.5, 3.5, 128)
     x[5, :] = np.float16(6e-8)
+    x[6, :] = rng.standard_normal(256).astype(np.float16)          # an infinite value per group:
+    x[6, 17], x[6, 200] = np.inf, -np.inf                          # scale +inf, every code 0
+    x[7, :128] = np.inf
+    x[7, 128:] = rng.standard_normal(128).astype(np.float16)
     _check_act(x)
 
 

@@ -24,8 +24,8 @@ def test_reciprocal_quotient_gives_identical_codes(tmp_path):
     out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=600)
     fields = out.stdout.split()
     got = dict(zip(fields[0::2], map(int, fields[1::2])))
-    # 0x7C00 amax values, each with 2 * (its index + 1) values v
-    n = 0x7C00
+    # amax bit patterns 0 .. 0x7C00 (+inf), each with 2 * (its index + 1) values v
+    n = 0x7C01
     assert got["pairs"] == n * (n + 1)
     assert got["code_mismatch"] == 0
     assert got["nonzero_mismatch"] == 0
