@@ -8,7 +8,7 @@
 // its DPP row, and lane t writes one 32-bit word of codes.  A 64-lane wave
 // covers 4 groups, so loads and stores are fully coalesced 256-byte / 64-byte
 // runs.  The kernel is HBM-bound: 2 bytes read, 0.5 byte written per element.
-#include "mq_internal.h"
+#include "gemm_common.h"
 
 namespace mq {
 namespace {
@@ -43,7 +43,52 @@ __global__ __launch_bounds__(256) void act_quant_kernel(const uint16_t* __restri
   if (t == 0) sa[m * G + j] = s;
 }
 
+// The same quantisation, written in the wide fragment order of the prefill
+// tile kernel (wide_a_index): codes as int8 16*q, so that kernel copies
+// them from memory to LDS without widening them.  One 16-lane team per
+// token, 16 consecutive tokens of one group per workgroup, so each 1 KB
+// fragment receives 256 contiguous bytes per workgroup.  Tokens in
+// [M, Mpad) (the last row block's padding) get codes 0 and no scale.
+__global__ __launch_bounds__(256) void act_quant_wide_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                             int64_t K, int64_t ldx, uint8_t* __restrict__ qaw,
+                                                             float* __restrict__ sa, int64_t Mpad) {
+  const int64_t m = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int t = threadIdx.x & 15;
+  if (m >= Mpad) return;  // whole 16-lane teams leave together
+  const int64_t G = K / kGroup;
+  const int64_t j = blockIdx.y;
+  float f[8];
+  if (m < M) {
+    unpack_h8(*reinterpret_cast<const uint4*>(x + m * ldx + j * kGroup + t * 8), f);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = row16_max(amax);
+  const float s = amax / 7.0f;
+  const float r = s == 0.0f ? 0.0f : 1.0f / s;
+  const uint32_t w = quant4_word(f, s, r);  // codes 8t .. 8t+7, low nibble first
+  // lane t holds codes 8t .. 8t+7: step t/4, half (t%4)/2, the first or
+  // second 8 bytes of that lane chunk: even codes, then odd codes, as 16*q
+  uint2 v;
+  v.x = (w << 4) & 0xF0F0F0F0u;
+  v.y = w & 0xF0F0F0F0u;
+  *reinterpret_cast<uint2*>(qaw + wide_a_index(m, j, G, t >> 2, (t >> 1) & 1) + (t & 1) * 8) = v;
+  if (t == 0 && m < M) sa[m * G + j] = s;
+}
+
 }  // namespace
+
+hipError_t launch_act_quant_wide(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* qaw,
+                                 float* sa, hipStream_t st) {
+  const int64_t Mpad = wide_rows(M);
+  hipLaunchKernelGGL(act_quant_wide_kernel, dim3((unsigned)(Mpad / 16), (unsigned)(K / kGroup)), dim3(256), 0,
+                     st, x, M, K, ldx, qaw, sa, Mpad);
+  return hipGetLastError();
+}
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             uint8_t* qa, float* sa, hipStream_t st) {

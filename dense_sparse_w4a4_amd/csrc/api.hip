@@ -137,6 +137,8 @@ mq_status mq_pack_weights(const uint16_t* w, int64_t N, int64_t K, int32_t block
                     "mq_pack_weights launch");
 }
 
+static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
 // Split-K partials of the tile kernel: [splits][M][N] fp32 when M > 32 and
 // the tiles alone would leave compute units idle; 0 otherwise.
 static size_t split_workspace(int64_t M, int64_t N, int64_t K) {
@@ -145,11 +147,24 @@ static size_t split_workspace(int64_t M, int64_t N, int64_t K) {
   return ks > 1 ? (size_t)ks * (size_t)M * (size_t)N * sizeof(float) : 0;
 }
 
+// Activation codes in the tile kernel's wide fragment order (M > 32):
+// one byte per code for ceil(M/32)*32 rows.
+static size_t wide_workspace(int64_t M, int64_t K) {
+  if (M <= 32 || K < kGroup) return 0;
+  return round256((size_t)wide_rows(M) * (size_t)K);
+}
+
+// mq_fused_gemm's workspace: the wide activation codes, then the split-K
+// partials.
+static size_t gemm_workspace(int64_t M, int64_t N, int64_t K) {
+  return wide_workspace(M, K) + split_workspace(M, N, K);
+}
+
 mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   g_err[0] = 0;
   MQ_REQUIRE(bytes, MQ_ERR_NULL_PTR, "bytes must be non-NULL");
   MQ_REQUIRE(M >= 0 && N >= 0 && K >= 0, MQ_ERR_SHAPE, "sizes must be >= 0");
-  *bytes = split_workspace(M, N, K);
+  *bytes = gemm_workspace(M, N, K);
   return MQ_OK;
 }
 
@@ -204,23 +219,38 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
   a.y = y;
   a.ldy = ldy;
   a.acc_dump = (flags & MQ_FLAG_DUMP_ACC) ? acc_dump : nullptr;
-  // split-K only with a large enough workspace; otherwise one pass over K
-  const size_t need = split_workspace(M, N, K);
-  const bool split = need > 0 && workspace && workspace_bytes >= need && aligned16(workspace);
-  a.part = split ? static_cast<float*>(workspace) : nullptr;
-  a.ksplit = split ? tile_gemm_splits(M, N, K) : 1;
+  // With the whole workspace (tile kernel route, M > 32): the codes are
+  // copied once into the wide fragment order, which the tile kernel moves
+  // to LDS without widening, and the split-K schedule is used where it
+  // applies.  Otherwise one pass over K from the packed codes.
+  const size_t need = gemm_workspace(M, N, K);
+  const bool wide = need > 0 && workspace && workspace_bytes >= need && M > 32 && tile_gemm_fits(a);
+  if (wide) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const mq_status st = hip_status(launch_widen_acts(qa, M, K, ws, (hipStream_t)stream),
+                                    "mq_fused_gemm widen launch");
+    if (st != MQ_OK) return st;
+    a.qaw = ws;
+    const size_t split = split_workspace(M, N, K);
+    a.part = split > 0 ? reinterpret_cast<float*>(ws + wide_workspace(M, K)) : nullptr;
+    a.ksplit = split > 0 ? tile_gemm_splits(M, N, K) : 1;
+  } else {
+    a.ksplit = 1;
+  }
   return hip_status(launch_fused_gemm(a, (hipStream_t)stream), "mq_fused_gemm launch");
 }
 
-static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
-
 // Workspace of mq_fused_layer: none when the streaming kernel quantises the
-// activations itself; otherwise the codes and scales of mq_quantize_act,
-// then the fused GEMM's split-K partials.
+// activations itself; otherwise the activation codes (packed [M][K/2] for
+// the streaming kernel, M <= 32; the wide fragment order for the tile
+// kernel, M > 32, whose area also holds the packed codes when the tile
+// kernel does not apply), their scales, then the split-K partials.
+static size_t layer_codes_bytes(int64_t M, int64_t K) {
+  return M > 32 ? wide_workspace(M, K) : round256((size_t)M * (size_t)(K / 2));
+}
 static size_t layer_workspace(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < kGroup || stream_quant_fits(M, N, K)) return 0;
-  return round256((size_t)M * (size_t)(K / 2)) + round256((size_t)M * (size_t)(K / kGroup) * 4) +
-         split_workspace(M, N, K);
+  return layer_codes_bytes(M, K) + round256((size_t)M * (size_t)(K / kGroup) * 4) + split_workspace(M, N, K);
 }
 
 mq_status mq_fused_layer_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes) {
@@ -307,17 +337,25 @@ static mq_status layer_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
     a.ldx = ldx;
     return hip_status(launch_fused_gemm(a, st), "mq_fused_layer launch");
   }
-  uint8_t* qa = ws;
-  float* sa = reinterpret_cast<float*>(ws + round256((size_t)M * (size_t)(K / 2)));
-  const mq_status s = hip_status(launch_act_quant(x, M, K, ldx, qa, sa, st),
-                                 "mq_fused_layer act-quant launch");
-  if (s != MQ_OK) return s;
-  a.qa = qa;
+  float* sa = reinterpret_cast<float*>(ws + layer_codes_bytes(M, K));
   a.sa = sa;
-  const size_t split = split_workspace(M, N, K);
-  if (split > 0) {
-    a.part = reinterpret_cast<float*>(ws + need - split);
-    a.ksplit = tile_gemm_splits(M, N, K);
+  if (M > 32 && tile_gemm_fits(a)) {
+    // tile kernel: codes quantised straight into the wide fragment order
+    const mq_status s = hip_status(launch_act_quant_wide(x, M, K, ldx, ws, sa, st),
+                                   "mq_fused_layer act-quant launch");
+    if (s != MQ_OK) return s;
+    a.qaw = ws;
+    const size_t split = split_workspace(M, N, K);
+    if (split > 0) {
+      a.part = reinterpret_cast<float*>(ws + need - split);
+      a.ksplit = tile_gemm_splits(M, N, K);
+    }
+  } else {
+    // streaming kernel: packed codes
+    const mq_status s = hip_status(launch_act_quant(x, M, K, ldx, ws, sa, st),
+                                   "mq_fused_layer act-quant launch");
+    if (s != MQ_OK) return s;
+    a.qa = ws;
   }
   return hip_status(launch_fused_gemm(a, st), "mq_fused_layer launch");
 }

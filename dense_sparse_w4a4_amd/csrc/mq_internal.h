@@ -84,6 +84,19 @@ __device__ __forceinline__ uint32_t quant4_word(const float f[8], float s, float
   return s < __builtin_inff() ? pack8(q) : 0u;
 }
 
+// Wide activation layout of the prefill tile kernel: int8 codes 16*q in the
+// kernel's MFMA fragment order, uint8 [Mpad/32][G][4][64][16].  For token m
+// (row block m/32, row r = m%32), group j, 32-channel step t and half h, the
+// 16 bytes at [m/32][j][t][r + 32h] hold the codes 32t + 16h + (0, 2, 4, 6,
+// 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15) of the group (the order widen8
+// gives for 8 packed bytes), so one row block's group is 4 KB contiguous
+// and each 1 KB step fragment is copied to LDS as it is.  Rows past M (up to
+// Mpad, a multiple of 32) hold zeros.
+__host__ __device__ constexpr int64_t wide_rows(int64_t M) { return (M + 31) / 32 * 32; }
+__host__ __device__ inline int64_t wide_a_index(int64_t m, int64_t j, int64_t G, int t, int h) {
+  return (((m >> 5) * G + j) * 4 + t) * 1024 + ((m & 31) + 32 * h) * 16;
+}
+
 // Eight fp16 values held in a uint4 -> floats.
 __device__ __forceinline__ void unpack_h8(const uint4& v, float f[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -106,6 +119,12 @@ mq_status fail(mq_status s, const char* fmt, ...);
 
 hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                             uint8_t* qa, float* sa, hipStream_t st);
+
+// Activation quantisation written in the prefill tile kernel's wide
+// fragment order (int8 codes, [ceil(M/32)][K/128][4][64][16] bytes) plus the
+// fp32 scales [M][K/128].
+hipError_t launch_act_quant_wide(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* qaw,
+                                 float* sa, hipStream_t st);
 
 hipError_t launch_select(const uint16_t* w, const uint16_t* xc, int64_t N, int64_t K,
                          int64_t T, int block, int n_select, int32_t* selected,
@@ -135,6 +154,9 @@ struct GemmArgs {
   int ksplit;         // K splits of the tile kernel (1 = none)
   const uint16_t* x;  // fp16 activations [M][ldx] to quantise in the streaming
   int64_t ldx;        // kernel (qa, sa unused), or null
+  const uint8_t* qaw; // tile kernel: activation codes in the wide fragment order
+                      // (wide_a_index), copied to LDS as they are, or null
+                      // (packed qa, widened while staged)
 };
 
 // In-kernel activation quantisation of the streaming kernel: at most
@@ -172,5 +194,7 @@ hipError_t launch_mfma_rate(int blocks, int iters, int64_t* cycles, int32_t* sin
 bool tile_gemm_fits(const GemmArgs& a);
 int tile_gemm_splits(int64_t M, int64_t N, int64_t K);  // K splits the tile kernel would use
 hipError_t launch_tile_gemm(const GemmArgs& a, hipStream_t st);
+// Packed activation codes qa [M][K/2] -> the wide fragment order.
+hipError_t launch_widen_acts(const uint8_t* qa, int64_t M, int64_t K, uint8_t* qaw, hipStream_t st);
 
 }  // namespace mq

@@ -59,7 +59,7 @@ _SIGS = {
                                               _c_i32, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
 }
 
-NOALLOC_SCRATCH_BYTES = 64 << 20
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 _lib = None
 

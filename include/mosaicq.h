@@ -236,8 +236,8 @@ mq_status mq_fused_layer(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, i
                          uint16_t* y, int64_t ldy, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* Device scratch of mq_fused_layer_noalloc, per device: 64 MiB. */
-#define MQ_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+/* Device scratch of mq_fused_layer_noalloc, per device: 128 MiB. */
+#define MQ_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
 
 /*
  * mq_fused_layer for callers that cannot allocate device memory (code under

@@ -213,7 +213,7 @@ def test_fused_layer_noalloc_validation(L):
     assert call(x=None) == NULLP
     assert call(x=PMIS) == ALIGN
     assert call(M=0, x=None, y=None) == OK
-    # a shape whose workspace passes the 64 MiB scratch is refused before any
+    # a shape whose workspace passes the 128 MiB scratch is refused before any
     # device call
     assert call(M=8192, K=25600, ldx=25600, N=128, ldy=128, ns=0) == WS
     assert "scratch" in ops.last_error()

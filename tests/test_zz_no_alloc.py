@@ -63,7 +63,7 @@ def test_noalloc_matches_fused_layer(seq):
 
 
 def test_noalloc_refuses_shapes_beyond_the_scratch():
-    # M x K whose codes alone pass 64 MiB: refused before anything is enqueued
+    # M x K whose codes alone pass 128 MiB: refused before anything is enqueued
     K, N, M = 25600, 128, 8192
     assert ops.fused_layer_workspace(M, N, K) > ops.NOALLOC_SCRATCH_BYTES
     x = torch.zeros((M, K), dtype=torch.float16, device="cuda")
