@@ -112,6 +112,85 @@ mq_status mq_select_blocks(const uint16_t* w, const uint16_t* x_calib, int64_t N
                     "mq_select_blocks launch");
 }
 
+// Shape rules shared by the exact-distortion entry points.
+static mq_status exact_check(int64_t N, int64_t K, int64_t T, int32_t block) {
+  MQ_REQUIRE(valid_block(block), MQ_ERR_BLOCK, "block = %d must be 32, 64 or 128", block);
+  MQ_REQUIRE(N > 0 && N % block == 0, MQ_ERR_SHAPE, "N = %lld must be a positive multiple of %d",
+             (long long)N, block);
+  MQ_REQUIRE(K > 0 && K % kGroup == 0, MQ_ERR_SHAPE, "K = %lld must be a positive multiple of 128",
+             (long long)K);
+  MQ_REQUIRE(T >= 0 && T < ((int64_t)1 << 22), MQ_ERR_SHAPE, "T = %lld outside [0, 2^22)",
+             (long long)T);
+  const int64_t B = (N / block) * (K / block);
+  MQ_REQUIRE(B < ((int64_t)1 << 24), MQ_ERR_SHAPE, "too many blocks (%lld >= 2^24)", (long long)B);
+  MQ_REQUIRE(N * K < ((int64_t)1 << 36) && T * N < ((int64_t)1 << 36), MQ_ERR_SHAPE,
+             "N x K or T x N too large");
+  return MQ_OK;
+}
+
+mq_status mq_select_exact_workspace(int64_t N, int64_t K, int64_t T, int32_t block, size_t* bytes) {
+  g_err[0] = 0;
+  MQ_REQUIRE(bytes, MQ_ERR_NULL_PTR, "bytes must be non-NULL");
+  const mq_status s = exact_check(N, K, T, block);
+  if (s != MQ_OK) return s;
+  *bytes = exact_greedy_workspace(N, K, T, block);
+  return MQ_OK;
+}
+
+mq_status mq_select_exact_greedy(const uint16_t* w, const uint16_t* x_calib, int64_t N, int64_t K,
+                                 int64_t T, int32_t block, int32_t n_select, int32_t* selected,
+                                 int32_t* order, double* gains, double* dist, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const mq_status s = exact_check(N, K, T, block);
+  if (s != MQ_OK) return s;
+  const int64_t B = (N / block) * (K / block);
+  MQ_REQUIRE(n_select >= 0 && n_select <= B, MQ_ERR_BUDGET, "n_select = %d outside [0, %lld]",
+             n_select, (long long)B);
+  MQ_REQUIRE(w && workspace, MQ_ERR_NULL_PTR, "w and workspace must be non-NULL");
+  MQ_REQUIRE(T == 0 || x_calib, MQ_ERR_NULL_PTR, "x_calib must be non-NULL when T > 0");
+  MQ_REQUIRE(n_select == 0 || selected, MQ_ERR_NULL_PTR, "selected must be non-NULL");
+  MQ_REQUIRE(aligned16(w) && aligned16(x_calib) && aligned16(selected) && aligned16(order) &&
+                 aligned16(gains) && aligned16(dist) && aligned16(workspace),
+             MQ_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = exact_greedy_workspace(N, K, T, block);
+  MQ_REQUIRE(workspace_bytes >= need, MQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
+             workspace_bytes, need);
+  return hip_status(launch_exact_greedy(w, x_calib, N, K, T, block, n_select, selected, order,
+                                        gains, dist, workspace, (hipStream_t)stream),
+                    "mq_select_exact_greedy launch");
+}
+
+mq_status mq_distortion_workspace(int64_t N, int64_t K, int64_t T, int32_t block, size_t* bytes) {
+  g_err[0] = 0;
+  MQ_REQUIRE(bytes, MQ_ERR_NULL_PTR, "bytes must be non-NULL");
+  const mq_status s = exact_check(N, K, T, block);
+  if (s != MQ_OK) return s;
+  *bytes = distortion_workspace(N, K, T, block);
+  return MQ_OK;
+}
+
+mq_status mq_distortion(const uint16_t* w, const uint16_t* x, int64_t N, int64_t K, int64_t T,
+                        int32_t block, const int32_t* selected, int32_t n_selected, double* dist,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = 0;
+  const mq_status s = exact_check(N, K, T, block);
+  if (s != MQ_OK) return s;
+  MQ_REQUIRE(n_selected >= 0, MQ_ERR_BUDGET, "n_selected = %d must be >= 0", n_selected);
+  MQ_REQUIRE(w && dist && workspace, MQ_ERR_NULL_PTR, "w, dist and workspace must be non-NULL");
+  MQ_REQUIRE(T == 0 || x, MQ_ERR_NULL_PTR, "x must be non-NULL when T > 0");
+  MQ_REQUIRE(n_selected == 0 || selected, MQ_ERR_NULL_PTR, "selected must be non-NULL");
+  MQ_REQUIRE(aligned16(w) && aligned16(x) && aligned16(selected) && aligned16(dist) &&
+                 aligned16(workspace),
+             MQ_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t need = distortion_workspace(N, K, T, block);
+  MQ_REQUIRE(workspace_bytes >= need, MQ_ERR_WORKSPACE, "workspace %zu bytes < %zu needed",
+             workspace_bytes, need);
+  return hip_status(launch_distortion(w, x, N, K, T, block, selected, n_selected, dist, workspace,
+                                      (hipStream_t)stream),
+                    "mq_distortion launch");
+}
+
 mq_status mq_pack_weights(const uint16_t* w, int64_t N, int64_t K, int32_t block,
                           const int32_t* selected, int32_t n_select, uint8_t* qw, uint16_t* sw,
                           int32_t* row_ptr, int32_t* col_idx, uint8_t* qr, uint16_t* sr,

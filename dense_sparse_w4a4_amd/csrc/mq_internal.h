@@ -130,6 +130,17 @@ hipError_t launch_select(const uint16_t* w, const uint16_t* xc, int64_t N, int64
                          int64_t T, int block, int n_select, int32_t* selected,
                          double* delta, double* hdiag, hipStream_t st);
 
+// Exact output distortion and the greedy selection by it (offline study of
+// the Delta-score); workspaces in bytes for the given shape.
+size_t exact_greedy_workspace(int64_t N, int64_t K, int64_t T, int b);
+size_t distortion_workspace(int64_t N, int64_t K, int64_t T, int b);
+hipError_t launch_exact_greedy(const uint16_t* w, const uint16_t* x, int64_t N, int64_t K,
+                               int64_t T, int b, int n_select, int32_t* selected, int32_t* order,
+                               double* gains, double* dist, void* ws, hipStream_t st);
+hipError_t launch_distortion(const uint16_t* w, const uint16_t* x, int64_t N, int64_t K,
+                             int64_t T, int b, const int32_t* ids, int64_t n_ids, double* dist,
+                             void* ws, hipStream_t st);
+
 hipError_t launch_pack(const uint16_t* w, int64_t N, int64_t K, int block,
                        const int32_t* selected, int n_select, uint8_t* qw, uint16_t* sw,
                        int32_t* row_ptr, int32_t* col_idx, uint8_t* qr, uint16_t* sr,

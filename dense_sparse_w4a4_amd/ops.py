@@ -55,6 +55,14 @@ _SIGS = {
     "mq_smooth_weights": (ctypes.c_int, [_vp, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp, _vp, _vp, _vp]),
     "mq_smooth_acts": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _vp]),
     "mq_measure_mfma": (ctypes.c_int, [_c_i32, _c_i32, _vp, _vp, _vp]),
+    "mq_distortion_workspace": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, _c_i32,
+                                               ctypes.POINTER(ctypes.c_size_t)]),
+    "mq_distortion": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32, _vp, _c_i32, _vp,
+                                     _vp, ctypes.c_size_t, _vp]),
+    "mq_select_exact_workspace": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, _c_i32,
+                                                 ctypes.POINTER(ctypes.c_size_t)]),
+    "mq_select_exact_greedy": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _c_i32, _c_i32,
+                                              _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "mq_fused_layer_noalloc": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i32,
                                               _c_i32, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
 }
@@ -174,6 +182,61 @@ def select_blocks(w: torch.Tensor, x_calib: torch.Tensor, block: int, n_select: 
         _ptr(w), _ptr(x_calib) if T else None, N, K, T, block, n_select,
         _ptr(sel) if n_select else None, _ptr(delta), _ptr(H), _stream(stream)))
     return sel, delta[:B], H
+
+
+def _exact_ws(fn: str, N: int, K: int, T: int, block: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check(fn, getattr(lib(), fn)(N, K, T, block, ctypes.byref(n)))
+    return int(n.value)
+
+
+@_on_stream
+def distortion(w: torch.Tensor, x: torch.Tensor, block: int, selected: torch.Tensor,
+               stream=None) -> torch.Tensor:
+    """Exact output distortion ||X (W - deq Q - R_S)^T||_F^2 (fp64 [1] device)."""
+    _dev(w, torch.float16, "w")
+    _dev(x, torch.float16, "x")
+    _dev(selected, torch.int32, "selected")
+    w, x, selected = w.contiguous(), x.contiguous(), selected.contiguous()
+    N, K = w.shape
+    T = x.shape[0]
+    if x.shape[1] != K:
+        raise ValueError("x must have K columns")
+    ws = torch.empty(max(_exact_ws("mq_distortion_workspace", N, K, T, block), 1),
+                     dtype=torch.uint8, device=w.device)
+    out = torch.empty(1, dtype=torch.float64, device=w.device)
+    n = int(selected.numel())
+    _check("mq_distortion", lib().mq_distortion(
+        _ptr(w), _ptr(x) if T else None, N, K, T, block, _ptr(selected) if n else None, n,
+        _ptr(out), _ptr(ws), ws.numel(), _stream(stream)))
+    return out
+
+
+@_on_stream
+def select_exact_greedy(w: torch.Tensor, x_calib: torch.Tensor, block: int, n_select: int,
+                        stream=None):
+    """Greedy selection by exact output distortion.  Returns (selected int32
+    [n_select] ascending, order int32 [n_select] as picked, gains fp64
+    [n_select], dist fp64 [2] = D({}), D(selected) on x_calib)."""
+    _dev(w, torch.float16, "w")
+    _dev(x_calib, torch.float16, "x_calib")
+    w, x_calib = w.contiguous(), x_calib.contiguous()
+    N, K = w.shape
+    T = x_calib.shape[0]
+    if x_calib.shape[1] != K:
+        raise ValueError("x_calib must have K columns")
+    ws = torch.empty(max(_exact_ws("mq_select_exact_workspace", N, K, T, block), 1),
+                     dtype=torch.uint8, device=w.device)
+    k = max(n_select, 0)
+    sel = torch.empty(k, dtype=torch.int32, device=w.device)
+    order = torch.empty(k, dtype=torch.int32, device=w.device)
+    gains = torch.empty(k, dtype=torch.float64, device=w.device)
+    dist = torch.empty(2, dtype=torch.float64, device=w.device)
+    _check("mq_select_exact_greedy", lib().mq_select_exact_greedy(
+        _ptr(w), _ptr(x_calib) if T else None, N, K, T, block, n_select,
+        _ptr(sel) if k else None, _ptr(order) if k else None, _ptr(gains) if k else None,
+        _ptr(dist), _ptr(ws), ws.numel(), _stream(stream)))
+    return sel, order, gains, dist
 
 
 @dataclass

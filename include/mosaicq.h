@@ -147,6 +147,59 @@ mq_status mq_pack_weights(const uint16_t* w, int64_t N, int64_t K, int32_t block
                           int32_t* col_idx, uint8_t* qr, uint16_t* sr,
                           void* stream);
 
+/*
+ * Exact output distortion of a selection (offline study of the Delta-score).
+ *   D(S) = || X (W - deq Q(W) - sum_{i in S} R_hat_i)^T ||_F^2   in fp64,
+ * with Q, E = W - deq Q(W) and R_hat exactly as in mq_select_blocks (R_hat of
+ * block i is its candidate residual whether or not i is in S).
+ * [summary-pt Metodologia 2 and Principais Contribuicoes 2: the Delta-score
+ * replaces this costly exact evaluation of the output distortion.]
+ *   w        : fp16 [N][K];  x: fp16 [T][K] (the tokens D is measured on)
+ *   N % block == 0, K % 128 == 0, 0 <= T < 2^22, block in {32, 64, 128},
+ *   (N/block)*(K/block) < 2^24, N*K and T*N < 2^36
+ *   selected : int32 [n_selected] block ids; ids outside [0, B) are
+ *              ignored and a repeated id counts once
+ *   dist     : fp64 [1] (device output)
+ *   workspace: device buffer of mq_distortion_workspace's bytes (16-byte
+ *              aligned), about 8*N*K bytes; the caller owns it
+ * The sum runs in a fixed order, so repeated calls give identical bits.
+ */
+mq_status mq_distortion_workspace(int64_t N, int64_t K, int64_t T, int32_t block, size_t* bytes);
+mq_status mq_distortion(const uint16_t* w, const uint16_t* x, int64_t N, int64_t K, int64_t T,
+                        int32_t block, const int32_t* selected, int32_t n_selected, double* dist,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Greedy selection by exact output distortion (offline study of the
+ * Delta-score; the packed layer does not use it).  Starting from S = {},
+ * n_select times: every unchosen block (nt, kt) has the gain
+ *   gain = ||o||^2 - ||o - X[:, kt-block] R_hat_(nt,kt)^T||^2
+ * where o = X (E - R_S)^T on the block's output rows nt*block .. +block-1;
+ * the block of largest gain joins S (ties: lower id; a NaN gain ranks
+ * below every number).  A pick changes only its own row's outputs, so
+ * only that row's candidates are evaluated again.  fp64 throughout; each
+ * gain sums per 64-token tile, then over tiles in order.
+ * [summary-pt Metodologia 2 and Principais Contribuicoes 2, as above.]
+ *   w, x_calib, shape rules: as mq_distortion; 0 <= n_select <= B
+ *   selected : int32 [n_select] chosen ids, ascending (output)
+ *   order    : int32 [n_select] the same ids in the order picked (output,
+ *              may be NULL)
+ *   gains    : fp64 [n_select] each pick's gain when picked (output, may
+ *              be NULL)
+ *   dist     : fp64 [2] D({}) and D(S) on x_calib (output, may be NULL)
+ *   workspace: device buffer of mq_select_exact_workspace's bytes (16-byte
+ *              aligned), about 12*N*K + 8*T*N bytes; the caller owns it
+ * Every step runs on `stream` with no host synchronisation: one pick
+ * kernel, one update of the picked row's outputs and one re-evaluation
+ * of that row per step.
+ */
+mq_status mq_select_exact_workspace(int64_t N, int64_t K, int64_t T, int32_t block,
+                                    size_t* bytes);
+mq_status mq_select_exact_greedy(const uint16_t* w, const uint16_t* x_calib, int64_t N, int64_t K,
+                                 int64_t T, int32_t block, int32_t n_select, int32_t* selected,
+                                 int32_t* order, double* gains, double* dist, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
 /* Debug flag for mq_fused_gemm: also store the exact integer accumulators. */
 #define MQ_FLAG_DUMP_ACC 1u
 

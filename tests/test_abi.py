@@ -217,3 +217,53 @@ def test_fused_layer_noalloc_validation(L):
     # device call
     assert call(M=8192, K=25600, ldx=25600, N=128, ldy=128, ns=0) == WS
     assert "scratch" in ops.last_error()
+
+
+def test_exact_selection_validation(L):
+    n = ctypes.c_size_t(0)
+    fw = L.mq_select_exact_workspace
+    assert fw(512, 512, 128, 64, ctypes.byref(n)) == OK
+    # rem fp64 + R_hat fp32 per weight, outputs fp64 per (token, output), and
+    # per-block gains, tile partials, flags, order and pick gains
+    assert n.value >= 12 * 512 * 512 + 8 * 128 * 512 + 64 * (8 + 2 * 2 * 8 + 1 + 4 + 8)
+    assert fw(512, 512, 128, 48, ctypes.byref(n)) == BLOCK
+    assert fw(500, 512, 128, 64, ctypes.byref(n)) == SHAPE
+    assert fw(512, 512, 1 << 22, 64, ctypes.byref(n)) == SHAPE
+    assert fw(1 << 17, 1 << 17, 8, 32, ctypes.byref(n)) == SHAPE   # 2^24 blocks
+    assert fw(512, 512, 128, 64, None) == NULLP
+
+    g = L.mq_select_exact_greedy
+
+    def call(**kw):
+        a = dict(w=P, x=P, N=512, K=512, T=128, b=64, ns=6, sel=P, order=None, gains=None,
+                 dist=None, ws=P, wsb=1 << 30)
+        a.update(kw)
+        return g(a["w"], a["x"], a["N"], a["K"], a["T"], a["b"], a["ns"], a["sel"], a["order"],
+                 a["gains"], a["dist"], a["ws"], a["wsb"], None)
+    assert call(b=100) == BLOCK
+    assert call(K=500) == SHAPE
+    assert call(ns=65) == BUDGET
+    assert call(ns=-1) == BUDGET
+    assert call(w=None) == NULLP
+    assert call(x=None) == NULLP
+    assert call(sel=None) == NULLP
+    assert call(ws=None) == NULLP
+    assert call(order=PMIS) == ALIGN
+    assert call(wsb=1024) == WS
+
+    d = L.mq_distortion
+    fd = L.mq_distortion_workspace
+    assert fd(512, 512, 128, 64, ctypes.byref(n)) == OK and n.value >= 8 * 512 * 512
+
+    def dcall(**kw):
+        a = dict(w=P, x=P, N=512, K=512, T=128, b=64, sel=P, ns=6, dist=P, ws=P, wsb=1 << 30)
+        a.update(kw)
+        return d(a["w"], a["x"], a["N"], a["K"], a["T"], a["b"], a["sel"], a["ns"], a["dist"],
+                 a["ws"], a["wsb"], None)
+    assert dcall(b=16) == BLOCK
+    assert dcall(N=96) == SHAPE
+    assert dcall(ns=-2) == BUDGET
+    assert dcall(sel=None) == NULLP
+    assert dcall(dist=None) == NULLP
+    assert dcall(x=PMIS) == ALIGN
+    assert dcall(wsb=4096) == WS
