@@ -118,7 +118,7 @@ def traffic_from_profile(wname: str, kernel: str):
         return None
     d = json.load(open(p))
     from dense_sparse_w4a4_amd.profiling import kernel_sources_sha
-    if d.get("sources_sha") != kernel_sources_sha() or d.get("kernel") != kernel:
+    if d.get("sources_sha") != kernel_sources_sha(kernel) or d.get("kernel") != kernel:
         return None
     return d.get("bytes_per_launch")
 

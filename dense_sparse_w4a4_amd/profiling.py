@@ -27,14 +27,34 @@ COPY_BYTES = 256 << 20
 COPY_KERNEL = "copyBuffer"
 
 
-def kernel_sources_sha() -> str:
-    """Hash of every file under csrc/ (the kernels and their launchers)."""
-    h = hashlib.sha256()
+# the sources a fused-GEMM kernel's code and launch configuration come from
+KERNEL_SOURCES = {
+    "gemm_stream_kernel": ["gemm.hip"],
+    "gemm_tile_kernel": ["gemm_tile.hip"],
+}
+SHARED_SOURCES = ["api.hip", "gemm_common.h", "mq_internal.h"]
+
+
+def kernel_sources_sha(kernel: str | None = None) -> str:
+    """Hash of the sources `kernel` is built and launched from (every file
+    under csrc/ when the kernel is not one of the fused-GEMM kernels)."""
     csrc = os.path.join(PKG, "csrc")
-    for f in sorted(os.listdir(csrc)):
+    if kernel in KERNEL_SOURCES:
+        files = sorted(KERNEL_SOURCES[kernel] + SHARED_SOURCES)
+    else:
+        files = sorted(os.listdir(csrc))
+    h = hashlib.sha256()
+    for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def _stamp(kernel: str | None = None) -> str:
+    """Where a summary comes from: the commit named by MQ_COMMIT (the GPU
+    host has the tree, not the history) and the kernel sources' hash."""
+    c = os.environ.get("MQ_COMMIT", "unrecorded")
+    return f"Taken on commit {c}; kernel sources sha {kernel_sources_sha(kernel)}."
 
 
 def _one(pattern: str) -> str:
@@ -63,8 +83,8 @@ def _pct(v, q: float) -> float:
 def stats(outdir: str, prefix: str, title: str, cmd: str) -> str:
     rows = list(csv.DictReader(open(_one(os.path.join(outdir, f"{prefix}_kernel_stats.csv")))))
     trace = list(csv.DictReader(open(_one(os.path.join(outdir, f"{prefix}_kernel_trace.csv")))))
-    out = [f"# {title}", "", "Command (from the repository root on the GPU host):", "", "```", cmd, "```", "",
-           "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---:|---:|---:|---:|---:|"]
+    out = [f"# {title}", "", _stamp(), "", "Command (from the repository root on the GPU host):", "", "```", cmd,
+           "```", "", "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---:|---:|---:|---:|---:|"]
     for r in rows[:12]:
         out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f}% |")
@@ -131,7 +151,8 @@ def traffic(fetch_dir: str, write_dir: str, workload: str, kernel: str, cmd: str
     return {
         "workload": workload,
         "kernel": kernel,
-        "sources_sha": kernel_sources_sha(),
+        "sources_sha": kernel_sources_sha(kernel),
+        "commit": os.environ.get("MQ_COMMIT", "unrecorded"),
         "dispatches": len(f_k),
         "fetch_kib_per_dispatch": round(fetch_kib, 1),
         "write_kib_per_dispatch": round(write_kib, 1),
@@ -169,7 +190,8 @@ def sq(dirs, workload: str, kernel: str, cmd: str) -> str:
     if not vals:
         raise SystemExit(f"no dispatch of a kernel containing '{kernel}'")
     m = {k: sum(v) / len(v) for k, v in vals.items()}
-    out = [f"# SQ counters, `{kernel}`, workload {workload}", "", "Commands (from the repository root on the GPU host):", "",
+    out = [f"# SQ counters, `{kernel}`, workload {workload}", "", _stamp(kernel), "",
+           "Commands (from the repository root on the GPU host):", "",
            "```", cmd, "```", "",
            "| counter | mean per dispatch | dispatches |", "|---|---:|---:|"]
     for k in sorted(m):
