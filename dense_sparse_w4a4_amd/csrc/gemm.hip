@@ -43,11 +43,14 @@ namespace {
 // group and get scale 0), so the load counters are waited on exactly, and
 // the per-lane offsets are fixed: each unit only moves uniform bases.  The
 // tile's activation and weight scales are staged in LDS once.  The residual
-// blocks of the tile's block row follow as a second stream with the same
-// item work against the activation fragment of each block's group (the
-// zipper); they are dealt round-robin to the waves, so the waves finish
-// together however the selected blocks cluster in K, and the first two are
-// loaded before the dense stream starts.
+// blocks of the tile's block row form a second stream of items against the
+// activation fragment of each block's group (the zipper); they are dealt
+// round-robin to the waves, so the waves finish together however the
+// selected blocks cluster in K.  A wave's first two entries are loaded in
+// the prologue beside the first dense units and processed before the dense
+// stream, whose run then hides the loads of the next two; any further
+// entries follow the dense stream.  A block of edge <= 64 is one MFMA per
+// slab on 8-byte operands (only the block's bytes are loaded).
 //
 // QP > 0 (M <= kStreamQuantRows, one token tile): the activations arrive as
 // fp16 and the workgroup quantises them itself before the streams start (the
@@ -120,10 +123,8 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   // one item of slab s: two MFMAs, then y += (sa/256 * sc) * acc for the
   // lane's tokens (sc = the item's weight or residual row scale, 0 for
   // padding)
-  auto item = [&](int s, const uint4& W, const uint4& X, float sc, uint32_t rm, int j, bool valid,
-                  int64_t dump_at, bool dump_res) {
-    v4i acc = mfma(widen8(X.x, X.y), widen8(W.x & rm, W.y & rm), zero);
-    acc = mfma(widen8(X.z, X.w), widen8(W.z & rm, W.w & rm), acc);
+  auto scale_add = [&](int s, const v4i& acc, float sc, int j, bool valid, int64_t dump_at,
+                       bool dump_res) {
     const float4 s4 = *reinterpret_cast<const float4*>(sa_t + j * 16 + 4 * ch);
     y[s][0] = fmaf(s4.x * sc, (float)acc[0], y[s][0]);
     y[s][1] = fmaf(s4.y * sc, (float)acc[1], y[s][1]);
@@ -141,6 +142,12 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
         }
       }
     }
+  };
+  auto item = [&](int s, const uint4& W, const uint4& X, float sc, uint32_t rm, int j, bool valid,
+                  int64_t dump_at, bool dump_res) {
+    v4i acc = mfma(widen8(X.x, X.y), widen8(W.x & rm, W.y & rm), zero);
+    acc = mfma(widen8(X.z, X.w), widen8(W.z & rm, W.w & rm), acc);
+    scale_add(s, acc, sc, j, valid, dump_at, dump_res);
   };
   auto compute_dense = [&](const Unit& D, int t) {
 #pragma unroll
@@ -233,12 +240,19 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   // weight codes and scales), so the prologue's load counters are waited on
   // exactly; later entries are loaded only when they exist, so no load is
   // left in flight at the end ----
+  // A block of edge b <= 64 is one MFMA per slab: lane chunk c carries the
+  // block's channels [16c, 16c + 16) (8 packed bytes of the activation row
+  // and of the residual row, chunks past the block edge masked), so its
+  // item loads only the block's bytes.  b = 128 covers the whole group and
+  // takes the dense items' operand layout (16 bytes, two MFMAs).
+  constexpr bool kHalf = BLK <= 64;
   struct Res {
-    uint4 W[NS];
-    uint4 X;
+    uint4 W[NS];  // kHalf: .x, .y
+    uint4 X;      // kHalf: .x, .y
     uint32_t S[NS];
     uint32_t rm;
     int j;
+    int xo;       // kHalf: byte offset of the lane's activation codes in the group
   };
   // (an entry whose block column is outside [0, K/b) contributes nothing:
   // its codes are masked and its group index clipped)
@@ -249,16 +263,36 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
     const int e = has ? rp0 + wave + KS * k : 0;
     R.j = kt * BLK / kGroup;
     const int lo = kt * BLK - R.j * kGroup;
-    const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK) && okt;
-    R.rm = act ? 0xFFFFFFFFu : 0u;
+    if constexpr (kHalf) {
+      const bool act = 16 * ch < BLK && okt;
+      R.rm = act ? 0xFFFFFFFFu : 0u;
+      R.xo = (lo + (act ? 16 * ch : 0)) / 2;
 #pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      R.W[s] = ld16(has ? a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + 16 * s + r16) * (BLK / 2) +
-                              (act ? 16 * ch - lo / 2 : 0)
-                        : a.qw + offW);
-      R.S[s] = *(has ? a.sr + (int64_t)e * BLK + rrow + 16 * s + r16 : a.sw);
+      for (int s = 0; s < NS; ++s) {
+        const uint2 v = *reinterpret_cast<const uint2*>(
+            has ? a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + 16 * s + r16) * (BLK / 2) + (act ? 8 * ch : 0)
+                : a.qw + offW);
+        R.W[s].x = v.x;
+        R.W[s].y = v.y;
+        R.S[s] = *(has ? a.sr + (int64_t)e * BLK + rrow + 16 * s + r16 : a.sw);
+      }
+      if constexpr (QP == 0) {
+        const uint2 v = *reinterpret_cast<const uint2*>(a.qa + (int64_t)R.j * 64 + offX - ch * 16 + R.xo);
+        R.X.x = v.x;
+        R.X.y = v.y;
+      }
+    } else {
+      const bool act = (32 * ch >= lo) && (32 * ch < lo + BLK) && okt;
+      R.rm = act ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        R.W[s] = ld16(has ? a.qr + (int64_t)e * (BLK * BLK / 2) + (rrow + 16 * s + r16) * (BLK / 2) +
+                                (act ? 16 * ch - lo / 2 : 0)
+                          : a.qw + offW);
+        R.S[s] = *(has ? a.sr + (int64_t)e * BLK + rrow + 16 * s + r16 : a.sw);
+      }
+      if constexpr (QP == 0) R.X = ld16(a.qa + (int64_t)R.j * 64 + offX);
     }
-    if constexpr (QP == 0) R.X = ld16(a.qa + (int64_t)R.j * 64 + offX);
   };
   // the first two entries are loaded now, before the scale staging, so they
   // arrive during the dense stream
@@ -316,12 +350,39 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
 
   auto res_item = [&](int k, const Res& R) {
     const int64_t e = rp0 + wave + KS * k;
-    const uint4 X = QP > 0 ? lds_x(R.j) : R.X;
+    if constexpr (kHalf) {
+      uint2 X;
+      if constexpr (QP > 0) {
+        X = *reinterpret_cast<const uint2*>(qa_t + offXl - ch * 16 + R.j * 64 + R.xo);
+      } else {
+        X = make_uint2(R.X.x, R.X.y);
+      }
+      const v4i xa = widen8(X.x, X.y);
 #pragma unroll
-    for (int s = 0; s < NS; ++s)
-      item(s, R.W[s], X, h2f((uint16_t)R.S[s]), R.rm, R.j, true,
-           a.M * a.N * G + e * a.M * BLK + rrow + 16 * s + r16, true);
+      for (int s = 0; s < NS; ++s) {
+        const v4i acc = mfma(xa, widen8(R.W[s].x & R.rm, R.W[s].y & R.rm), zero);
+        scale_add(s, acc, h2f((uint16_t)R.S[s]), R.j, true, a.M * a.N * G + e * a.M * BLK + rrow + 16 * s + r16,
+                  true);
+      }
+    } else {
+      const uint4 X = QP > 0 ? lds_x(R.j) : R.X;
+#pragma unroll
+      for (int s = 0; s < NS; ++s)
+        item(s, R.W[s], X, h2f((uint16_t)R.S[s]), R.rm, R.j, true,
+             a.M * a.N * G + e * a.M * BLK + rrow + 16 * s + r16, true);
+    }
   };
+  // ---- the wave's first two residual entries (loaded in the prologue,
+  // beside the first dense units), then the loads of the next two, which
+  // arrive while the dense stream runs ----
+  if (nres > 0) {
+    res_item(0, R0);
+    if (nres > 2) res_ptrs(2, res_kt(2), R0);
+    if (nres > 1) {
+      res_item(1, R1);
+      if (nres > 3) res_ptrs(3, res_kt(3), R1);
+    }
+  }
   // ---- dense stream (ping-pong buffers, never copied while in flight) ----
   for (int t = 0; t < nunits; t += 2) {
     compute_dense(U0, t);
@@ -333,7 +394,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
 
   // ---- residual stream: the same item work against the activation
   // fragment of each block's group, two entries in flight ----
-  for (int k = 0; k < nres; k += 2) {
+  for (int k = 2; k < nres; k += 2) {
     res_item(k, R0);
     if (k + 2 < nres) res_ptrs(k + 2, res_kt(k + 2), R0);
     if (k + 1 >= nres) break;
