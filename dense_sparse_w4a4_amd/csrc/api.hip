@@ -37,6 +37,22 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 static bool valid_block(int b) { return b == 32 || b == 64 || b == 128; }
 
+// Number of b x b blocks of an N x K matrix, or INT64_MAX when N or K is
+// 2^31 or more (so the callers' block-count limit rejects it without the
+// product overflowing).
+static int64_t block_count(int64_t N, int64_t K, int b) {
+  if (N >= ((int64_t)1 << 31) || K >= ((int64_t)1 << 31)) return INT64_MAX;
+  return (N / b) * (K / b);
+}
+
+// Sizes the fused GEMM accepts (each below 2^31, packed weights and
+// activations each below 4 GiB), checked without overflowing.
+static bool gemm_sizes_ok(int64_t M, int64_t N, int64_t K) {
+  const int64_t lim = (int64_t)1 << 31;
+  return M >= 0 && N >= 0 && K >= 0 && M < lim && N < lim && K < lim &&
+         N * (K / 2) < ((int64_t)1 << 32) && M * (K / 2) < ((int64_t)1 << 32);
+}
+
 }  // namespace mq
 
 using namespace mq;
@@ -75,8 +91,8 @@ mq_status mq_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, 
   MQ_REQUIRE(K > 0 && K % kGroup == 0, MQ_ERR_SHAPE, "K = %lld must be a positive multiple of 128",
              (long long)K);
   MQ_REQUIRE(ldx >= K, MQ_ERR_SHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
-  MQ_REQUIRE(M <= (int64_t)1 << 31 && M * (K / kGroup) < (int64_t)1 << 36, MQ_ERR_SHAPE,
-             "M x K too large");
+  MQ_REQUIRE(M <= (int64_t)1 << 31 && K < (int64_t)1 << 31 && M * (K / kGroup) < (int64_t)1 << 36,
+             MQ_ERR_SHAPE, "M x K too large");
   if (M == 0) return MQ_OK;
   MQ_REQUIRE(x && qa && sa, MQ_ERR_NULL_PTR, "x, qa and sa must be non-NULL");
   MQ_REQUIRE(ldx % 8 == 0, MQ_ERR_ALIGN, "ldx = %lld must be a multiple of 8", (long long)ldx);
@@ -96,8 +112,10 @@ mq_status mq_select_blocks(const uint16_t* w, const uint16_t* x_calib, int64_t N
   MQ_REQUIRE(K > 0 && K % kGroup == 0, MQ_ERR_SHAPE, "K = %lld must be a positive multiple of 128",
              (long long)K);
   MQ_REQUIRE(T >= 0, MQ_ERR_SHAPE, "T = %lld must be >= 0", (long long)T);
-  const int64_t B = (N / block) * (K / block);
+  const int64_t B = block_count(N, K, block);
   MQ_REQUIRE(B < ((int64_t)1 << 31), MQ_ERR_SHAPE, "too many blocks (%lld)", (long long)B);
+  MQ_REQUIRE(T < ((int64_t)1 << 31) && T * K < ((int64_t)1 << 40), MQ_ERR_SHAPE,
+             "T = %lld calibration tokens too many", (long long)T);
   MQ_REQUIRE(n_select >= 0 && n_select <= B, MQ_ERR_BUDGET, "n_select = %d outside [0, %lld]",
              n_select, (long long)B);
   MQ_REQUIRE(w && delta_out && hdiag_out, MQ_ERR_NULL_PTR,
@@ -121,7 +139,7 @@ static mq_status exact_check(int64_t N, int64_t K, int64_t T, int32_t block) {
              (long long)K);
   MQ_REQUIRE(T >= 0 && T < ((int64_t)1 << 22), MQ_ERR_SHAPE, "T = %lld outside [0, 2^22)",
              (long long)T);
-  const int64_t B = (N / block) * (K / block);
+  const int64_t B = block_count(N, K, block);
   MQ_REQUIRE(B < ((int64_t)1 << 24), MQ_ERR_SHAPE, "too many blocks (%lld >= 2^24)", (long long)B);
   MQ_REQUIRE(N * K < ((int64_t)1 << 36) && T * N < ((int64_t)1 << 36), MQ_ERR_SHAPE,
              "N x K or T x N too large");
@@ -144,7 +162,7 @@ mq_status mq_select_exact_greedy(const uint16_t* w, const uint16_t* x_calib, int
   g_err[0] = 0;
   const mq_status s = exact_check(N, K, T, block);
   if (s != MQ_OK) return s;
-  const int64_t B = (N / block) * (K / block);
+  const int64_t B = block_count(N, K, block);
   MQ_REQUIRE(n_select >= 0 && n_select <= B, MQ_ERR_BUDGET, "n_select = %d outside [0, %lld]",
              n_select, (long long)B);
   MQ_REQUIRE(w && workspace, MQ_ERR_NULL_PTR, "w and workspace must be non-NULL");
@@ -201,7 +219,7 @@ mq_status mq_pack_weights(const uint16_t* w, int64_t N, int64_t K, int32_t block
              (long long)N, block);
   MQ_REQUIRE(K > 0 && K % kGroup == 0, MQ_ERR_SHAPE, "K = %lld must be a positive multiple of 128",
              (long long)K);
-  const int64_t B = (N / block) * (K / block);
+  const int64_t B = block_count(N, K, block);
   MQ_REQUIRE(B < ((int64_t)1 << 31), MQ_ERR_SHAPE, "too many blocks (%lld)", (long long)B);
   MQ_REQUIRE(n_select >= 0 && n_select <= B, MQ_ERR_BUDGET, "n_select = %d outside [0, %lld]",
              n_select, (long long)B);
@@ -242,7 +260,8 @@ static size_t gemm_workspace(int64_t M, int64_t N, int64_t K) {
 mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   g_err[0] = 0;
   MQ_REQUIRE(bytes, MQ_ERR_NULL_PTR, "bytes must be non-NULL");
-  MQ_REQUIRE(M >= 0 && N >= 0 && K >= 0, MQ_ERR_SHAPE, "sizes must be >= 0");
+  MQ_REQUIRE(gemm_sizes_ok(M, N, K), MQ_ERR_SHAPE,
+             "sizes must be >= 0 and below 2^31, packed weights and activations below 4 GiB");
   *bytes = gemm_workspace(M, N, K);
   return MQ_OK;
 }
@@ -262,7 +281,7 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
   MQ_REQUIRE(K > 0 && K % kGroup == 0, MQ_ERR_SHAPE, "K = %lld must be a positive multiple of 128",
              (long long)K);
   MQ_REQUIRE(ldy >= N, MQ_ERR_SHAPE, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
-  const int64_t B = (N / block) * (K / block);
+  const int64_t B = block_count(N, K, block);
   MQ_REQUIRE(B < ((int64_t)1 << 31), MQ_ERR_SHAPE, "too many blocks (%lld)", (long long)B);
   MQ_REQUIRE(M < ((int64_t)1 << 31) && N < ((int64_t)1 << 31) && K < ((int64_t)1 << 31),
              MQ_ERR_SHAPE, "sizes must be below 2^31");
@@ -335,7 +354,8 @@ static size_t layer_workspace(int64_t M, int64_t N, int64_t K) {
 mq_status mq_fused_layer_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes) {
   g_err[0] = 0;
   MQ_REQUIRE(bytes, MQ_ERR_NULL_PTR, "bytes must be non-NULL");
-  MQ_REQUIRE(M >= 0 && N >= 0 && K >= 0, MQ_ERR_SHAPE, "sizes must be >= 0");
+  MQ_REQUIRE(gemm_sizes_ok(M, N, K), MQ_ERR_SHAPE,
+             "sizes must be >= 0 and below 2^31, packed weights and activations below 4 GiB");
   *bytes = layer_workspace(M, N, K);
   return MQ_OK;
 }
@@ -362,7 +382,7 @@ static mq_status layer_check(const uint16_t* x, int64_t M, int64_t K, int64_t ld
              (long long)K);
   MQ_REQUIRE(ldx >= K, MQ_ERR_SHAPE, "ldx = %lld < K = %lld", (long long)ldx, (long long)K);
   MQ_REQUIRE(ldy >= N, MQ_ERR_SHAPE, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
-  const int64_t B = (N / block) * (K / block);
+  const int64_t B = block_count(N, K, block);
   MQ_REQUIRE(B < ((int64_t)1 << 31), MQ_ERR_SHAPE, "too many blocks (%lld)", (long long)B);
   MQ_REQUIRE(M < ((int64_t)1 << 31) && N < ((int64_t)1 << 31) && K < ((int64_t)1 << 31),
              MQ_ERR_SHAPE, "sizes must be below 2^31");
@@ -524,7 +544,7 @@ mq_status mq_residual_merge(const uint8_t* qa, const float* sa, int64_t M, int64
   MQ_REQUIRE(K > 0 && K % kGroup == 0, MQ_ERR_SHAPE, "K = %lld must be a positive multiple of 128",
              (long long)K);
   MQ_REQUIRE(ldy >= N, MQ_ERR_SHAPE, "ldy = %lld < N = %lld", (long long)ldy, (long long)N);
-  const int64_t B = (N / block) * (K / block);
+  const int64_t B = block_count(N, K, block);
   MQ_REQUIRE(M < ((int64_t)1 << 31) && N < ((int64_t)1 << 31) && K < ((int64_t)1 << 31) &&
                  B < ((int64_t)1 << 31),
              MQ_ERR_SHAPE, "sizes must be below 2^31");
@@ -605,6 +625,9 @@ mq_status mq_validate_csr(const int32_t* row_ptr, const int32_t* col_idx, int64_
   MQ_REQUIRE(row_ptr, MQ_ERR_NULL_PTR, "row_ptr must be non-NULL");
   MQ_REQUIRE(n_select >= 0, MQ_ERR_BUDGET, "n_select must be >= 0");
   MQ_REQUIRE(n_select == 0 || col_idx, MQ_ERR_NULL_PTR, "col_idx must be non-NULL");
+  const int64_t B = block_count(N, K, block);
+  MQ_REQUIRE(B < ((int64_t)1 << 31), MQ_ERR_SHAPE, "too many blocks (%lld)", (long long)B);
+  MQ_REQUIRE(n_select <= B, MQ_ERR_BUDGET, "n_select = %d > %lld blocks", n_select, (long long)B);
   const int64_t NT = N / block, KT = K / block;
   std::vector<int32_t> rp(NT + 1), ci(n_select);
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);

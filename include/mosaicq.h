@@ -106,7 +106,8 @@ mq_status mq_quantize_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
  * [summary-pt Metodologia 2: Hessian-guided Delta-score weighting the
  * residual error by the input channels' diagonal Hessian; top-K blocks.]
  *   w        : fp16 [N][K];  x_calib: fp16 [T][K]
- *   N % block == 0, K % 128 == 0, T >= 0, block in {32, 64, 128},
+ *   N % block == 0, K % 128 == 0, block in {32, 64, 128},
+ *   0 <= T < 2^31 with T*K < 2^40,
  *   0 <= n_select <= (N/block)*(K/block), (N/block)*(K/block) < 2^31
  *   selected : int32 [n_select] (output; may be NULL when n_select == 0)
  *   delta_out: fp64 [(N/block)*(K/block)] (output, required: also used as
@@ -205,10 +206,13 @@ mq_status mq_select_exact_greedy(const uint16_t* w, const uint16_t* x_calib, int
 
 /*
  * Bytes of workspace mq_fused_gemm can use for this shape (host output).
- * Nonzero only for M > 32 when the 256 x 128 output tiles alone would leave
- * compute units idle: the K groups are then split over several workgroups,
- * which write fp32 partial outputs [splits][M][N] into the workspace, and a
- * second kernel sums them in split order (so y stays deterministic).
+ * Nonzero only for M > 32: the activation codes widened to int8 in the
+ * prefill kernel's fragment order (ceil(M/32)*32*K bytes, rounded up to
+ * 256), then, when the 256 x 128 output tiles alone would leave compute
+ * units idle, fp32 partial outputs [splits][M][N] of the K groups split
+ * over several workgroups, summed by a second kernel in split order (so y
+ * stays deterministic).  Sizes the GEMM does not accept (each below 2^31,
+ * packed weights and activations each below 4 GiB) give MQ_ERR_SHAPE.
  */
 mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes);
 
@@ -236,9 +240,12 @@ mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes
  *              unspecified but finite y.  Check a CSR with mq_validate_csr.
  *   y        : fp16 [M][ldy], ldy >= N, ldy % 8 == 0 (output)
  *   workspace: device buffer of workspace_bytes (16-byte aligned) or NULL.
- *              With at least mq_fused_gemm_workspace's bytes the split-K
- *              schedule is used; with less, or NULL, one pass over K (same
- *              result up to fp32 summation order, slower for such shapes).
+ *              With at least mq_fused_gemm_workspace's bytes (M > 32) the
+ *              codes are first widened into it for the prefill kernel and
+ *              the split-K schedule is used where it applies; with less, or
+ *              NULL, the kernel reads the packed codes in one pass over K
+ *              (same accumulators, y the same up to fp32 summation order,
+ *              slower).
  *              The call owns it until the stream has drained.
  *   Also:      N*K/2 and M*K/2 must each be below 2^32 (MQ_ERR_SHAPE).
  *   flags    : 0 or MQ_FLAG_DUMP_ACC
@@ -381,6 +388,8 @@ mq_status mq_measure_mfma(int32_t blocks, int32_t iters, int64_t* cycles, int32_
  * Synchronous CSR check (copies row_ptr and col_idx to the host and waits
  * for `stream`): row_ptr[0] == 0, non-decreasing, row_ptr[N/block] ==
  * n_select, col_idx strictly ascending within a row and < K/block.
+ * N and K below 2^31 with fewer than 2^31 blocks (MQ_ERR_SHAPE) and
+ * 0 <= n_select <= number of blocks (MQ_ERR_BUDGET) are checked first.
  * Returns MQ_OK or MQ_ERR_CSR.
  */
 mq_status mq_validate_csr(const int32_t* row_ptr, const int32_t* col_idx,
