@@ -172,8 +172,16 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
   const int tile = item - split * tiles;
   const int jb = (int)((int64_t)split * G / a.ksplit);        // this split's groups
   const int je = (int)((int64_t)(split + 1) * G / a.ksplit);  // [jb, je)
-  const int64_t m0 = (int64_t)(tile / tiles_n) * TBM;
-  const int64_t n0 = (int64_t)(tile % tiles_n) * TBN;
+  // Bands of kBand token tiles: consecutive tiles walk down a band's token
+  // tiles for one channel tile, then move to the next channel tile, so the
+  // workgroups an XCD runs together share weight tiles as well as token rows.
+  constexpr int kBand = 4;
+  const int tiles_m = tiles / tiles_n;
+  const int band = tile / (kBand * tiles_n);
+  const int bh = min(kBand, tiles_m - band * kBand);
+  const int rb = tile - band * kBand * tiles_n;
+  const int64_t m0 = (int64_t)(band * kBand + rb % bh) * TBM;
+  const int64_t n0 = (int64_t)(rb / bh) * TBN;
   const int64_t Kh = a.K / 2;
   const int nt0 = (int)(n0 / BLK);
   const int nrows_b = (int)(a.N / BLK);
