@@ -159,9 +159,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
   const int r16 = lane & 15;
   const int ch = lane >> 4;
 
-  // XCD-aware order: consecutive work items (same K split, same token rows,
-  // adjacent channel tiles) go to the same XCD so its L2 serves the shared
-  // A rows.  With split-K, work item = split * tiles + tile.
+  // XCD-aware order: consecutive work items (same K split, neighbouring
+  // tiles in the banded order below) go to the same XCD so its L2 serves
+  // the rows and weight tiles they share.  With split-K, work item =
+  // split * tiles + tile.
   const int tiles_n = (int)((a.N + TBN - 1) / TBN);
   const int items = (int)gridDim.x;
   const int tiles = items / a.ksplit;
