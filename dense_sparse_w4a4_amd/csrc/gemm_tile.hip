@@ -42,9 +42,10 @@
 //
 // Pipeline: group g passes through register buffer g%2 and LDS stage g%2.
 // While the waves compute group j from LDS, the loads of groups j+1 and j+2
-// are in flight.  Every step issues the same A, B and scale loads (groups
-// past the end re-read the last group), so the hardware load counters are
-// waited on exactly.  Within a group a wave runs its four sub-tiles one
+// are in flight.  Every step issues the same loads (activation DMA,
+// weight codes and scales, residual codes and row scales, the last from a
+// dummy offset where no block is selected; groups past the end re-read the
+// last group), so the hardware load counters are waited on exactly.  Within a group a wave runs its four sub-tiles one
 // after the other (scale product and int8 MFMAs, then the epilogue); the
 // two waves of each SIMD overlap one's MFMAs with the other's epilogue.
 #include "gemm_common.h"
@@ -269,14 +270,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
     } else {
       S.sc = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.sw) + j * 2 + offS);
     }
-    if (anyr[j]) {  // uniform: the tile has a selected block in group j
-      // (tab is zero-filled, so unguarded reads are safe)
-      const int entR = (int)tab[tabR + j * C::NBC];
-      const int entS = (int)tab[max(tabS, 0) + j * C::NBC];
-      S.R = ld16(rbase + (uint32_t)(entR > 0 ? entR * (BLK * BLK / 2) + baseR : 0));
-      const int es = tabS >= 0 ? entS : 0;
-      S.sr = *reinterpret_cast<const uint16_t*>(sbase + (uint32_t)(es > 0 ? es * (BLK * 2) + baseS : 0));
-    }
+    // residual codes and row scales: loaded in every step, from offset 0
+    // of a valid buffer where no block is selected (tab is zero-filled), so
+    // every step issues the same loads and the DMA wait below is exact
+    const int entR = (int)tab[tabR + j * C::NBC];
+    const int entS = (int)tab[max(tabS, 0) + j * C::NBC];
+    S.R = ld16(rbase + (uint32_t)(entR > 0 ? entR * (BLK * BLK / 2) + baseR : 0));
+    const int es = tabS >= 0 ? entS : 0;
+    S.sr = *reinterpret_cast<const uint16_t*>(sbase + (uint32_t)(es > 0 ? es * (BLK * 2) + baseS : 0));
   };
 
   // registers -> LDS stage, in four parts: widened operands in lane order,
@@ -463,10 +464,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
                                          16, 0, 0);
     }
   };
-  // after a step's loads: the step's DMA (issued before the at least two
-  // register loads of the step) has completed
+  // after a step's loads: the step's DMA (issued before the step's four
+  // register loads: weights, scale, residual codes, residual scale) has
+  // completed
   auto dma_wait = [&]() {
-    if constexpr (AW) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+    if constexpr (AW) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   };
 
   // Two LDS stages: group j is computed from stage j%2 while the waves
