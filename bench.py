@@ -292,7 +292,7 @@ def smooth_study(args):
 def exact_selection_study(args):
     """The Delta-score against the exact-distortion greedy selection it stands
     in for, on full-size Llama-3-8B projections (512 calibration tokens, the
-    block edges and budgets of the method).  Both selections, their exact
+    block edges and budgets of the method) and the Qwen3-32B MLP shapes.  Both selections, their exact
     output distortions on the calibration tokens and on 512 held-out tokens,
     and their GPU times come from the library; prints one JSON line."""
     import torch
@@ -309,11 +309,14 @@ def exact_selection_study(args):
         torch.cuda.synchronize()
         return out, a.elapsed_time(b)
 
-    cases = [((4096, 4096), 64, 0.10), ((4096, 4096), 32, 0.10), ((4096, 4096), 128, 0.10),
-             ((4096, 4096), 64, 0.05), ((4096, 4096), 64, 0.20), ((14336, 4096), 64, 0.10)]
+    cases = [("llama3-8b", (4096, 4096), 64, 0.10), ("llama3-8b", (4096, 4096), 32, 0.10),
+             ("llama3-8b", (4096, 4096), 128, 0.10), ("llama3-8b", (4096, 4096), 64, 0.05),
+             ("llama3-8b", (4096, 4096), 64, 0.20), ("llama3-8b", (14336, 4096), 64, 0.10),
+             ("qwen3-32b", (5120, 25600), 64, 0.10), ("qwen3-32b", (25600, 5120), 64, 0.10)]
     rows = []
-    for (K, N), b, rho in cases:
-        spec = syn.llama3_8b(K, N).with_block(b, rho)
+    for model, (K, N), b, rho in cases:
+        make = syn.llama3_8b if model == "llama3-8b" else syn.qwen3_32b
+        spec = make(K, N).with_block(b, rho)
         w = torch.from_numpy(syn.make_weight(spec)).to(dev)
         xc = torch.from_numpy(syn.make_calib(spec)).to(dev)
         xe = torch.from_numpy(syn.make_acts(spec, 512)).to(dev)
@@ -330,7 +333,7 @@ def exact_selection_study(args):
             d[tag] = dict(base=d0, greedy=dg, recovered_delta=round(1 - dd / d0, 5),
                           recovered_greedy=round(1 - dg / d0, 5))
         overlap = len(set(sd.tolist()) & set(sg.tolist())) / max(1, k)
-        row = dict(K=K, N=N, block=b, rho=rho, n_select=k, T=spec.T,
+        row = dict(model=model, K=K, N=N, block=b, rho=rho, n_select=k, T=spec.T,
                    recovered_calib_delta=d["calib"]["recovered_delta"],
                    recovered_calib_greedy=d["calib"]["recovered_greedy"],
                    recovered_holdout_delta=d["holdout"]["recovered_delta"],
@@ -343,14 +346,14 @@ def exact_selection_study(args):
                    # selection (different summation orders: equal to ~1e-12)
                    greedy_dist_rel_diff=float(f"{float(dist[1].item()) / d['calib']['greedy'] - 1:.3e}"))
         rows.append(row)
-        log(f"[exact] K={K} N={N} b={b} rho={rho:.2f} n={k}: recovered calib Delta "
+        log(f"[exact] {model} K={K} N={N} b={b} rho={rho:.2f} n={k}: recovered calib Delta "
             f"{row['recovered_calib_delta']:.4f} / greedy {row['recovered_calib_greedy']:.4f}, held-out "
             f"{row['recovered_holdout_delta']:.4f} / {row['recovered_holdout_greedy']:.4f}, overlap "
             f"{row['overlap']:.3f}, GPU {t_delta:.2f} ms / {t_greedy:.1f} ms")
         del w, xc, xe, sd, sg, gains, dist
         torch.cuda.empty_cache()
     print(json.dumps({"metric": "output distortion recovered: Delta top-K vs exact greedy",
-                      "workload": "llama3-8b-projections-T512", "data": "synthetic", "n_gpus": 1,
+                      "workload": "llama3-8b-and-qwen3-32b-projections-T512", "data": "synthetic", "n_gpus": 1,
                       "rows": rows}), flush=True)
 
 
