@@ -315,7 +315,13 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
     }
   };
 
-  const int wm = wave >> 1, wn = wave & 1;  // 64-row x 64-channel quarter of the tile
+  // Wave w computes the 64-token x 64-channel quarter (wm, wn) = (w % 4, w / 4)
+  // of the tile.  The hardware places waves w and w + 4 of a workgroup on one
+  // SIMD (measured with the hardware wave-id register), so every SIMD holds
+  // one wave of each 64-channel half: residual blocks, whose work falls on
+  // the waves of their own channels only, load all four SIMDs alike instead
+  // of two of them twice.
+  const int wm = wave & 3, wn = wave >> 2;
   float y[2][2][16];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
