@@ -469,6 +469,9 @@ hipError_t launch_stream_ns(const GemmArgs& a, const StreamPlan& p, hipStream_t 
 template <int BLK>
 hipError_t launch_blk(const GemmArgs& a, hipStream_t st) {
   const StreamPlan p = stream_plan(a.M, a.N, a.K, BLK, a.x != nullptr, a.acc_dump != nullptr);
+  if constexpr (BLK >= 64) {
+    if (p.ns == 4) return launch_stream_ns<BLK, 4>(a, p, st);
+  }
   if (p.ns == 2) return launch_stream_ns<BLK, 2>(a, p, st);
   return launch_stream_ns<BLK, 1>(a, p, st);
 }
@@ -538,6 +541,26 @@ static int long_run_waves(int64_t M, int64_t N, int64_t K, int block) {
   return (N / 32) * ((M + 15) / 16) >= 256 ? ks : 0;
 }
 
+// Four slabs (64 channels) per workgroup for several tokens (M > 4), where
+// the block edge allows it and the four-slab grid still spans every compute
+// unit, with the long-run rule's waves per tile.  Every workgroup reads its
+// token tile's activation fragments once (16 * K/2 bytes, from L2): at
+// M = 16 that is half the weight bytes again with two slabs and a quarter
+// with four.  Measured on Qwen3-32B 5120x25600, M = 16: 21.0 -> 19.7 us per
+// launch; neutral at M = 1, and slower wherever the grid would leave compute
+// units idle.  Returns the waves per tile, 0 when it does not apply.
+static int four_slab_waves(int64_t M, int64_t N, int64_t K, int block) {
+  if (M <= 4 || block < 64 || N % 64 != 0) return 0;
+  if ((N / 64) * ((M + 15) / 16) < 256) return 0;
+  const int64_t G = K / kGroup;
+  int ks = 16;
+  while (ks > 4 && G / ks < 8) ks /= 2;
+  if (G / ks < 8) return 0;
+  // (the tile's scale tables grow with the channels: very long K keeps the
+  // two-slab plan, whose tables still fit in LDS)
+  return stream_lds_bytes(K, ks, 0, 4) <= 160 * 1024 ? ks : 0;
+}
+
 StreamPlan stream_plan(int64_t M, int64_t N, int64_t K, int block, bool quantise, bool dump) {
   StreamPlan p;
   p.ns = dump ? 1 : stream_slabs(M, N, K, block);
@@ -546,6 +569,13 @@ StreamPlan stream_plan(int64_t M, int64_t N, int64_t K, int block, bool quantise
     const int ks = long_run_waves(M, N, K, block);
     if (ks > 0) {
       p.ns = 2;
+      p.ks = ks;
+    }
+  }
+  if (!dump && !quantise) {
+    const int ks = four_slab_waves(M, N, K, block);
+    if (ks > 0) {
+      p.ns = 4;
       p.ks = ks;
     }
   }

@@ -157,6 +157,9 @@ GEMM_CASES = [
     # uneven split-K: 25 groups over 3 splits of 8, 8 and 9 groups (an odd
     # count in the last split)
     (40, 128, 3200, 64, 0.10),
+    # streaming kernel with four 16-channel slabs per workgroup (M > 4 and
+    # 128 workgroups of 64 channels x two token tiles, the second ragged)
+    (20, 8192, 4096, 64, 0.10),
 ]
 
 
