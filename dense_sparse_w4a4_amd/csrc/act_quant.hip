@@ -80,7 +80,43 @@ __global__ __launch_bounds__(256) void act_quant_wide_kernel(const uint16_t* __r
   if (t == 0 && m < M) sa[m * G + j] = s;
 }
 
+// The same quantisation, written in 16-token tiles for the streaming kernel
+// (tiled_a_index): one workgroup per (tile, group) writes that group's 1 KB
+// of the tile, so every weight-stream step reads its activation codes as one
+// contiguous 1 KB instead of 64 bytes from each of 16 rows.  Tokens in
+// [M, Mpad) (the last tile's padding) get codes 0 and no scale.
+__global__ __launch_bounds__(256) void act_quant_tiled_kernel(const uint16_t* __restrict__ x, int64_t M,
+                                                              int64_t K, int64_t ldx, uint8_t* __restrict__ qat,
+                                                              float* __restrict__ sa) {
+  const int64_t m = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int t = threadIdx.x & 15;
+  const int64_t G = K / kGroup;
+  const int64_t j = blockIdx.y;
+  float f[8];
+  if (m < M) {
+    unpack_h8(*reinterpret_cast<const uint4*>(x + m * ldx + j * kGroup + t * 8), f);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = 0.0f;
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
+  amax = row16_max(amax);
+  const float s = amax / 7.0f;
+  const float r = s == 0.0f ? 0.0f : 1.0f / s;
+  *reinterpret_cast<uint32_t*>(qat + tiled_a_index(m, j, G) + t * 4) = quant4_word(f, s, r);
+  if (t == 0 && m < M) sa[m * G + j] = s;
+}
+
 }  // namespace
+
+hipError_t launch_act_quant_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* qat,
+                                  float* sa, hipStream_t st) {
+  hipLaunchKernelGGL(act_quant_tiled_kernel, dim3((unsigned)(tiled_rows(M) / 16), (unsigned)(K / kGroup)),
+                     dim3(256), 0, st, x, M, K, ldx, qat, sa);
+  return hipGetLastError();
+}
 
 hipError_t launch_act_quant_wide(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* qaw,
                                  float* sa, hipStream_t st) {

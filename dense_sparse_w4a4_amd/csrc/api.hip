@@ -339,12 +339,12 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
 }
 
 // Workspace of mq_fused_layer: none when the streaming kernel quantises the
-// activations itself; otherwise the activation codes (packed [M][K/2] for
-// the streaming kernel, M <= 32; the wide fragment order for the tile
-// kernel, M > 32, whose area also holds the packed codes when the tile
+// activations itself; otherwise the activation codes (packed, in 16-token
+// tiles, for the streaming kernel, M <= 32; the wide fragment order for the
+// tile kernel, M > 32, whose area also holds the tiled codes when the tile
 // kernel does not apply), their scales, then the split-K partials.
 static size_t layer_codes_bytes(int64_t M, int64_t K) {
-  return M > 32 ? wide_workspace(M, K) : round256((size_t)M * (size_t)(K / 2));
+  return M > 32 ? wide_workspace(M, K) : round256((size_t)tiled_rows(M) * (size_t)(K / 2));
 }
 static size_t layer_workspace(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < kGroup || stream_quant_fits(M, N, K)) return 0;
@@ -449,8 +449,15 @@ static mq_status layer_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
       a.part = reinterpret_cast<float*>(ws + need - split);
       a.ksplit = tile_gemm_splits(M, N, K);
     }
+  } else if (tiled_rows(M) * (K / 2) < ((int64_t)1 << 32)) {
+    // streaming kernel: packed codes in 16-token tiles (each group's codes
+    // of a tile one contiguous 1 KB)
+    const mq_status s = hip_status(launch_act_quant_tiled(x, M, K, ldx, ws, sa, st),
+                                   "mq_fused_layer act-quant launch");
+    if (s != MQ_OK) return s;
+    a.qat = ws;
   } else {
-    // streaming kernel: packed codes
+    // streaming kernel: packed codes, row-major
     const mq_status s = hip_status(launch_act_quant(x, M, K, ldx, ws, sa, st),
                                    "mq_fused_layer act-quant launch");
     if (s != MQ_OK) return s;

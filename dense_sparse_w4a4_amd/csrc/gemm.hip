@@ -88,14 +88,22 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
   const int gb = wave * G / KS;
   const int ng = (wave + 1) * G / KS - gb;
 
-  // per-lane byte offsets (32-bit: the host keeps N*K/2 and M*K/2 below 2^32)
+  // per-lane byte offsets (32-bit: the host keeps N*K/2, M*K/2 and the tiled
+  // codes' padded size below 2^32)
   // weight codes in the slab layout: each group of a slab is 1 KB, lane l's
   // 16 bytes at l*16, so every weight load of a wave reads 1 KB contiguous;
   // the workgroup's slabs are 16*K/2 bytes apart
   const uint32_t offW = (uint32_t)(n0 * Kh + lane * 16);
   const uint32_t slabW = (uint32_t)(16 * Kh);
   const int64_t mr = m0 + r16;  // token rows past M read row M-1 (computed, never stored)
-  const uint32_t offX = (uint32_t)((mr < a.M ? mr : a.M - 1) * Kh + ch * 16);
+  // activation codes: row-major qa (group j of token m at m*K/2 + 64j; rows
+  // past M read row M-1), or the 16-token tiles of qat (group j's codes of
+  // the tile in one contiguous 1 KB at 1024j from the tile's base)
+  const bool tiled = a.qat != nullptr;
+  const uint8_t* const xb = tiled ? a.qat : a.qa;
+  const int64_t xstep = tiled ? 1024 : 64;
+  const uint32_t offX = tiled ? (uint32_t)((m0 / 16) * G * 1024 + r16 * 64 + ch * 16)
+                              : (uint32_t)((mr < a.M ? mr : a.M - 1) * Kh + ch * 16);
   const int offXl = (int)((mr < a.M ? mr : a.M - 1) - m0) * qrow + ch * 16;  // QP > 0: in qa_t
   auto lds_x = [&](int j) { return *reinterpret_cast<const uint4*>(qa_t + offXl + j * 64); };
 
@@ -111,7 +119,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
       const int j = gb + min(t * U + u, ng - 1);
 #pragma unroll
       for (int s = 0; s < NS; ++s) D.W[u][s] = ld16(a.qw + (int64_t)j * 1024 + offW + s * slabW);
-      if constexpr (QP == 0) D.X[u] = ld16(a.qa + (int64_t)j * 64 + offX);
+      if constexpr (QP == 0) D.X[u] = ld16(xb + (int64_t)j * xstep + offX);
     }
   };
 
@@ -277,7 +285,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
         R.S[s] = *(has ? a.sr + (int64_t)e * BLK + rrow + 16 * s + r16 : a.sw);
       }
       if constexpr (QP == 0) {
-        const uint2 v = *reinterpret_cast<const uint2*>(a.qa + (int64_t)R.j * 64 + offX - ch * 16 + R.xo);
+        const uint2 v = *reinterpret_cast<const uint2*>(xb + (int64_t)R.j * xstep + offX - ch * 16 + R.xo);
         R.X.x = v.x;
         R.X.y = v.y;
       }
@@ -291,7 +299,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_stream_kernel(GemmArgs a) {
                           : a.qw + offW);
         R.S[s] = *(has ? a.sr + (int64_t)e * BLK + rrow + 16 * s + r16 : a.sw);
       }
-      if constexpr (QP == 0) R.X = ld16(a.qa + (int64_t)R.j * 64 + offX);
+      if constexpr (QP == 0) R.X = ld16(xb + (int64_t)R.j * xstep + offX);
     }
   };
   // the first two entries are loaded now, before the scale staging, so they

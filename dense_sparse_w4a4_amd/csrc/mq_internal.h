@@ -123,6 +123,14 @@ hipError_t launch_act_quant(const uint16_t* x, int64_t M, int64_t K, int64_t ldx
 // Activation quantisation written in the prefill tile kernel's wide
 // fragment order (int8 codes, [ceil(M/32)][K/128][4][64][16] bytes) plus the
 // fp32 scales [M][K/128].
+// Packed codes of token m, group j (64 bytes) in 16-token tiles: each
+// group's codes of a tile are one contiguous 1 KB, rows 64 bytes apart.
+__host__ __device__ inline int64_t tiled_a_index(int64_t m, int64_t j, int64_t G) {
+  return ((m >> 4) * G + j) * 1024 + (m & 15) * 64;
+}
+inline int64_t tiled_rows(int64_t M) { return (M + 15) / 16 * 16; }
+hipError_t launch_act_quant_tiled(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* qat,
+                                  float* sa, hipStream_t st);
 hipError_t launch_act_quant_wide(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* qaw,
                                  float* sa, hipStream_t st);
 
@@ -168,6 +176,8 @@ struct GemmArgs {
   const uint8_t* qaw; // tile kernel: activation codes in the wide fragment order
                       // (wide_a_index), copied to LDS as they are, or null
                       // (packed qa, widened while staged)
+  const uint8_t* qat; // streaming kernel: packed activation codes in 16-token
+                      // tiles (tiled_a_index), or null (qa row-major)
 };
 
 // In-kernel activation quantisation of the streaming kernel: at most

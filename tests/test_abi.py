@@ -154,11 +154,12 @@ def test_fused_layer_workspace_and_validation(L):
     for M in (1, 4):
         assert L.mq_fused_layer_workspace(M, 4096, 4096, ctypes.byref(n)) == OK
         assert n.value == 0
-    # otherwise codes [M][K/2] and scales [M][K/128] fp32, each rounded up to 256 bytes
+    # otherwise codes in 16-token tiles (M padded to a multiple of 16, K/2
+    # bytes per token) and scales [M][K/128] fp32, each rounded up to 256 bytes
     assert L.mq_fused_layer_workspace(16, 4096, 4096, ctypes.byref(n)) == OK
     assert n.value == 16 * 2048 + 16 * 32 * 4
     assert L.mq_fused_layer_workspace(5, 512, 640, ctypes.byref(n)) == OK
-    assert n.value == 1792 + 256
+    assert n.value == 16 * 320 + 256
     assert L.mq_fused_layer_workspace(4, 4096, 4096, None) == NULLP
     assert _layer_call(L, b=100) == BLOCK
     assert _layer_call(L, ldx=256) == SHAPE

@@ -51,6 +51,10 @@ CASES = [
     (5, 512, 512, 64, 0.10, False),
     (16, 256, 1024, 32, 0.10, False),
     (40, 384, 256, 128, 0.20, False),
+    # the two-kernel decode route reads its codes in 16-token tiles: a second,
+    # mostly padding tile, and a ragged one with 32-wide blocks
+    (17, 256, 1024, 64, 0.10, False),
+    (31, 128, 640, 32, 0.20, False),
 ]
 
 
