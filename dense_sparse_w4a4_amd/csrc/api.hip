@@ -449,9 +449,12 @@ static mq_status layer_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
       a.part = reinterpret_cast<float*>(ws + need - split);
       a.ksplit = tile_gemm_splits(M, N, K);
     }
-  } else if (tiled_rows(M) * (K / 2) < ((int64_t)1 << 32)) {
+  } else if (M > 8 && tiled_rows(M) * (K / 2) < ((int64_t)1 << 32)) {
     // streaming kernel: packed codes in 16-token tiles (each group's codes
-    // of a tile one contiguous 1 KB)
+    // of a tile one contiguous 1 KB: eight full cache lines instead of 64
+    // bytes from each of up to 16 rows; with 8 tokens or fewer the
+    // row-major codes touch no more lines than that, and the tile's padding
+    // rows would only add bytes)
     const mq_status s = hip_status(launch_act_quant_tiled(x, M, K, ldx, ws, sa, st),
                                    "mq_fused_layer act-quant launch");
     if (s != MQ_OK) return s;

@@ -267,8 +267,9 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
  * 0 when the decode kernel quantises the activations itself (M <= 4 and the
  * shape's (token, group) pairs fit its prologue); otherwise room for the
  * activation codes (in the layout the GEMM kernel reads best: 16-token tiles
- * for the decode kernel, M padded to a multiple of 16; the wide fragment
- * order for the prefill kernel), their scales and the split-K partials.
+ * for the decode kernel above 8 tokens, room for M padded to a multiple of
+ * 16 up to M = 32; the wide fragment order for the prefill kernel), their
+ * scales and the split-K partials.
  */
 mq_status mq_fused_layer_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes);
 
