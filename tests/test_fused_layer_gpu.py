@@ -107,13 +107,15 @@ def test_fused_layer_special_values_and_padded_rows():
         assert np.array_equal(host(sa).view(np.uint32), rsa.view(np.uint32))
 
 
-@pytest.mark.parametrize("K,N", syn.LLAMA3_8B_SHAPES)
-def test_fused_layer_full_size_decode(K, N):
-    # the launch configuration the benchmark times (M = 1 and 4 in one
-    # kernel, M = 16 through the workspace)
-    spec = syn.llama3_8b(K, N)
+@pytest.mark.parametrize("K,N,Ms", [(k, n, syn.LLAMA3_8B_DECODE_M) for k, n in syn.LLAMA3_8B_SHAPES] +
+                         [(k, n, [1, 16, 24]) for k, n in syn.QWEN3_32B_SHAPES])
+def test_fused_layer_full_size_decode(K, N, Ms):
+    # the launch configurations the benchmark times (M = 1 and 4 in one
+    # kernel, M = 16 through the workspace with the codes in 16-token tiles;
+    # M = 24 adds a ragged second tile)
+    spec = syn.llama3_8b(K, N) if (K, N) in syn.LLAMA3_8B_SHAPES else syn.qwen3_32b(K, N)
     w, xc, layer = _gpu_layer(spec, seed=0)
-    for M in syn.LLAMA3_8B_DECODE_M:
+    for M in Ms:
         print(f"K={K} N={N} M={M}", flush=True)
         xt = dev(syn.make_acts(spec, M))
         y = ops.fused_layer(xt, layer)
