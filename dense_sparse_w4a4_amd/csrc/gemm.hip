@@ -35,7 +35,9 @@ namespace {
 // wave order.  Activations are the MFMA A operand (rows = tokens), weights
 // the B operand (columns = channels): lane l owns channel l%16 of each slab
 // and tokens 4*(l/16) + i.  The slabs of a workgroup share one activation
-// fragment per group (and, with QP > 0, one in-prologue quantisation).
+// fragment per group (and, with QP > 0, one in-prologue quantisation).  The
+// codes come row-major (qa), or, on the layer route above 8 tokens, in
+// 16-token tiles (qat) where a group's fragment is one contiguous 1 KB.
 //
 // The run of dense groups is streamed in units of U groups with two units
 // in flight: the loads of unit t+2 are issued before unit t+1 is computed.
