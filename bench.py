@@ -5,7 +5,7 @@
 Default workload: the Qwen3-32B MLP shapes (K x N = 5120 x 25600 and
 25600 x 5120, 10% residual in 64 x 64 blocks) at M = 1, 16, 256 and 4096 -
 decode-shaped launches bounded by HBM and prefill-shaped launches bounded by
-the int8 matrix cores in one step.  One step is one pass of the online hot
+the matrix cores in one step.  One step is one pass of the online hot
 path - fp16 activations to fp16 y through mq_fused_layer (activation
 quantisation and the fused GEMM; one kernel where the GEMM quantises the
 token tile itself, else the act-quant kernel then the fused GEMM) - for every
@@ -20,14 +20,18 @@ Printed JSON (one line on stdout):
   value      algorithmic integer ops of the step / step time (TOP/s)
   gbs        algorithmic bytes of the step (fp16 X, packed layer, fp16 Y of
              every (shape, M)) / step time
-  roofline   per GEMM kernel (streaming kernel for M <= 32, tile kernel
-             above), the dominant one (most time per step) first:
-             algorithmic bytes (streaming: HBM) or ops (tile: int8 MFMA) per
+  roofline   per GEMM kernel (streaming kernel for M <= 32; tile kernel,
+             int8 route, for 32 < M < 1024; tile kernel, fp6 route, from
+             M = 1024), the dominant one (most time per step) first:
+             algorithmic bytes (streaming: HBM) or ops (tile: against the
+             dense peak of the matrix-core type it runs on, int8 or fp6) per
              launch / average launch time, from HIP events around K replays
              of a graph holding only that kernel's launches of the step (the
              one-kernel layer where it applies: its bytes count the fp16
-             activations it reads instead of codes); next to the measured
-             int8 matrix-core rate, shader clock and device-copy rate
+             activations it reads instead of codes; the fp6 kernel on its
+             operand images prepared outside the timing, while the step's
+             layer converts them on every call); next to the measured int8
+             matrix-core rate, shader clock and device-copy rate
   per_pair   per (shape, M): fused GEMM launch time p10 / median / p90 over
              replays, TOPS, GB/s, roofline fractions, the same kernel with an
              empty CSR (residual cost), act-quant alone, the whole layer
@@ -51,6 +55,8 @@ sys.path.insert(0, ROOT)
 METRIC = "fused W4A4+10% residual GEMM TOPS & HBM GB/s vs roofline, M=1..4096"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 INT8_MFMA_PEAK_TOPS = 5000.0   # MI355X dense int8 MFMA
+FP6_MFMA_PEAK_TOPS = 10100.0   # MI355X dense fp6 / fp4 MFMA
+FP6_MIN_M = 1024               # the library's fp6 route: M >= 1024, block 64 or 128
 ROTATE_BYTES = 512 << 20
 
 
@@ -83,10 +89,18 @@ def workload(name: str):
     raise SystemExit(f"unknown workload {name}")
 
 
-def kernel_of(M: int) -> str:
+def kernel_of(M: int, block: int = 64) -> str:
     """The GEMM kernel the library runs for M tokens (the streaming kernel up
-    to 32 tokens, the LDS-tiled kernel above)."""
-    return "gemm_stream_kernel" if M <= 32 else "gemm_tile_kernel"
+    to 32 tokens, the LDS-tiled kernel above: its fp6 route from 1024 tokens
+    with 64- or 128-wide blocks, its int8 route otherwise)."""
+    if M <= 32:
+        return "gemm_stream_kernel"
+    return "gemm_tile6_kernel" if M >= FP6_MIN_M and block in (64, 128) else "gemm_tile_kernel"
+
+
+def mfma_peak(kernel: str) -> float:
+    """Dense MFMA peak of the matrix-core type a tile kernel runs on."""
+    return FP6_MFMA_PEAK_TOPS if kernel == "gemm_tile6_kernel" else INT8_MFMA_PEAK_TOPS
 
 
 def weight_bytes(N, K, b, ns):
@@ -471,11 +485,19 @@ def main():
                 ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
                 gwsb = ops.fused_gemm_workspace(M, spec.N, spec.K)
                 gws = torch.empty(max(gwsb, 1), dtype=torch.uint8, device=dev)
-                s.append((spec, M, L, x, qa, sa, y, ws, gws))
+                f6 = None
+                if kernel_of(M, spec.block) == "gemm_tile6_kernel":
+                    # the fp6 kernel alone: its operand images prepared here,
+                    # outside every timed region (the step's mq_fused_layer
+                    # converts them itself on every call)
+                    _, _, pb = ops.fp6_sizes(M, spec.N, spec.K, spec.block, spec.n_select)
+                    f6 = (ops.fp6_prepare_acts(qa, spec.K), ops.fp6_prepare_weights(L),
+                          torch.empty(max(pb, 1), dtype=torch.uint8, device=dev))
+                s.append((spec, M, L, x, qa, sa, y, ws, gws, f6))
         sets.append(s)
     # pairs the layer runs as one kernel (the GEMM quantises the token tile)
     one_kernel = [ops.fused_layer_workspace(M, s.N, s.K) == 0 for s, M in pairs]
-    kern = [kernel_of(M) for _, M in pairs]
+    kern = [kernel_of(M, s.block) for s, M in pairs]
     torch.cuda.synchronize()
     log(f"[bench] workload {args.workload}: {len(pairs)} (shape, M) pairs per step, "
         f"{R} rotating copies x {step_footprint / 2**20:.1f} MiB, setup {time.perf_counter() - t0:.1f}s")
@@ -492,12 +514,14 @@ def main():
         # which=None: the step (mq_fused_layer for every pair); otherwise the
         # GEMM launches of the pairs whose kernel is `which` (the one-kernel
         # layer where it applies, else the fused GEMM from precomputed codes)
-        for p_idx, (spec, M, L, x, qa, sa, y, ws, gws) in enumerate(sets[i % R]):
+        for p_idx, (spec, M, L, x, qa, sa, y, ws, gws, f6) in enumerate(sets[i % R]):
             if which is None:
                 ops.fused_layer(x, L, out=y, workspace=ws)
             elif kern[p_idx] == which:
                 if one_kernel[p_idx]:
                     ops.fused_layer(x, L, out=y, workspace=ws)
+                elif f6 is not None:
+                    ops.fused_gemm_fp6(f6[0], sa, M, L, f6[1], out=y, split_ws=f6[2])
                 else:
                     ops.fused_gemm(qa, sa, L, out=y, workspace=gws)
 
@@ -563,21 +587,32 @@ def main():
     if use_graph and not args.no_per_pair:
         modes = ["fused", "dense", "actq", "layer"] + (["unfused"] if args.ablation else [])
         for p_idx, (spec, M) in enumerate(pairs):
-            (_, _, L0, x, qa, sa, y, ws, gws) = sets[0][p_idx]
+            (_, _, L0, x, qa, sa, y, ws, gws, f6) = sets[0][p_idx]
             n = max(2, -(-ROTATE_BYTES // L0.nbytes()))
             copies = [L0.clone() for _ in range(n)]
+            # the fp6 kernel reads prepared images: one per copy, so its
+            # launches rotate through as many weight bytes as the others
+            imgs = [ops.fp6_prepare_weights(L) for L in copies] if f6 is not None else None
+            if f6 is not None:
+                dimgs = [ops.fp6_prepare_weights(ops.PackedLayer(L.N, L.K, L.block, L.qw, L.sw,
+                                                                 torch.zeros_like(L.row_ptr), L.col_idx[:0],
+                                                                 L.qr[:0], L.sr[:0])) for L in copies]
             q2, s2 = torch.empty_like(qa), torch.empty_like(sa)
             res = {}
             for mode in modes:
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
-                    for L in copies:
+                    for ci, L in enumerate(copies):
                         D = ops.PackedLayer(L.N, L.K, L.block, L.qw, L.sw, torch.zeros_like(L.row_ptr),
                                             L.col_idx[:0], L.qr[:0], L.sr[:0])
                         if mode == "layer":
                             ops.fused_layer(x, L, out=y, workspace=ws)
                         elif mode == "actq":
                             ops.quantize_act(x, q2, s2)
+                        elif f6 is not None and mode in ("fused", "dense"):
+                            ops.fused_gemm_fp6(f6[0], sa, M, L if mode == "fused" else D,
+                                               imgs[ci] if mode == "fused" else dimgs[ci], out=y,
+                                               split_ws=f6[2])
                         else:
                             ops.fused_gemm(qa, sa, L if mode == "fused" else D, out=y, workspace=gws)
                         if mode == "unfused":
@@ -594,7 +629,9 @@ def main():
                     samples.append(e0.elapsed_time(e1) * 1e3 / n)
                 res[mode] = samples
                 del g
-            del copies
+            del copies, imgs
+            if f6 is not None:
+                del dimgs
             torch.cuda.empty_cache()
             med = {m: _pct(v, 50) for m, v in res.items()}
             gb = gemm_bytes(M, spec.N, spec.K, spec.block, spec.n_select)
@@ -605,7 +642,8 @@ def main():
                        tops=round(go / (med["fused"] * 1e-6) / 1e12, 2),
                        dense_equiv_tops=round(2 * M * spec.N * spec.K / (med["fused"] * 1e-6) / 1e12, 2),
                        gbs=round(gb / (med["fused"] * 1e-6) / 1e9, 1),
-                       frac_mfma=round(go / (med["fused"] * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
+                       frac_mfma=round(go / (med["fused"] * 1e-6) / 1e12 / mfma_peak(kern[p_idx]), 4),
+                       frac_int8_peak=round(go / (med["fused"] * 1e-6) / 1e12 / INT8_MFMA_PEAK_TOPS, 4),
                        frac_hbm=round(gb / (med["fused"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
                        dense_only_us_p50=round(med["dense"], 3),
                        residual_cost=round(med["fused"] / med["dense"] - 1, 4),
@@ -618,7 +656,8 @@ def main():
             per_pair.append(row)
             log(f"[bench]   K={spec.K:6d} N={spec.N:6d} M={M:5d}: gemm p50 {med['fused']:9.2f} us "
                 f"(p10 {row['us_p10']:.2f}, p90 {row['us_p90']:.2f})  {row['gbs']:8.1f} GB/s "
-                f"({row['frac_hbm']:5.1%} HBM)  {row['tops']:8.1f} TOPS ({row['frac_mfma']:5.1%} int8)  "
+                f"({row['frac_hbm']:5.1%} HBM)  {row['tops']:8.1f} TOPS ({row['frac_mfma']:5.1%} of "
+                f"{'fp6' if kern[p_idx] == 'gemm_tile6_kernel' else 'int8'} peak, {row['frac_int8_peak']:5.1%} int8)  "
                 f"dense-only {med['dense']:9.2f} us (residual +{row['residual_cost']:5.1%})  "
                 f"act-quant {med['actq']:7.2f} us  layer {med['layer']:9.2f} us"
                 + (f"  unfused x{row['unfused_over_fused']:.3f}" if "unfused" in med else ""))
@@ -635,8 +674,13 @@ def main():
                      frac=round(achieved / HBM_PEAK_GBS, 4))
         else:
             achieved = sum(launch_ops[i] for i in idx) / t / 1e12
-            r = dict(bound="mfma", achieved=round(achieved, 2), peak=INT8_MFMA_PEAK_TOPS, unit="TOP/s",
-                     frac=round(achieved / INT8_MFMA_PEAK_TOPS, 4))
+            r = dict(bound="mfma", achieved=round(achieved, 2), peak=mfma_peak(c), unit="TOP/s",
+                     frac=round(achieved / mfma_peak(c), 4))
+            if c == "gemm_tile6_kernel":
+                r["mfma_dtype"] = "fp6 e2m3 (int4 codes as exact fp6 fields), fp32 accumulate"
+                r["frac_of_int8_peak"] = round(achieved / INT8_MFMA_PEAK_TOPS, 4)
+            else:
+                r["mfma_dtype"] = "int8 (int4 codes widened), int32 accumulate"
         r["traffic"] = traffic_from_profile(args.workload, c)
         r["kernel"] = c
         r["launches_per_step"] = nl
@@ -653,7 +697,7 @@ def main():
         roof["other_kernels"] = [roof_of(c) for c in order[1:]]
     if not args.copy_calibration:
         roof.update(measure_mfma_ceiling(torch, ops))
-        if roof["bound"] == "mfma":
+        if roof["bound"] == "mfma" and roof["kernel"] == "gemm_tile_kernel":
             roof["frac_of_measured_mfma"] = round(roof["achieved"] / roof["measured_mfma_int8_tops"], 4)
         # a plain device copy measured here (outside the timed region): the
         # rate a streaming kernel reaches on this part, beside the datasheet
@@ -695,14 +739,16 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": "int4 codes on int8 / fp6 MFMA",
         "data": "synthetic",
         "config": {
             "workload": args.workload,
             "shapes_KxN": [[s.K, s.N] for s, _, _, _ in base],
             "M": sorted({M for _, M in pairs}),
             "group": 128, "block": base[0][0].block, "rho": base[0][0].rho,
-            "codes": "w4a4 int4 symmetric, int8 MFMA, int32 accumulators, fp32 epilogue, fp16 out",
+            "codes": ("w4a4 int4 symmetric; M <= 32: int8 MFMA, int32 accumulators; 32 < M < 1024: int8 MFMA; "
+                      "M >= 1024: exact fp6 MFMA on re-encoded codes (converted per call), fp32 group sums; "
+                      "fp32 epilogue, fp16 out"),
             "step": "mq_fused_layer (fp16 X -> fp16 Y) for every (shape, M)",
             "bytes_per_step": per_step_bytes, "ops_per_step": per_step_ops,
             "rotating_copies": R,

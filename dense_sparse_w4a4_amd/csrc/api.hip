@@ -236,6 +236,15 @@ mq_status mq_pack_weights(const uint16_t* w, int64_t N, int64_t K, int32_t block
 
 static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
+// The fp6 route converts the base weights and the residual blocks on every
+// call (one pass over their codes, about 1.9 bytes moved per weight); its
+// kernel saves about a fifth of the int8 route's time, which outweighs the
+// conversion from about 1000 tokens on (measured on the Qwen3-32B MLP
+// shapes: at M = 256 the conversion costs more than it saves).
+constexpr int64_t kFp6MinM = 1024;
+// (MQ_FLAG_FP6_TILE lowers it to the tile kernel's M > 32 for checks.)
+
+
 // Split-K partials of the tile kernel: [splits][M][N] fp32 when M > 32 and
 // the tiles alone would leave compute units idle; 0 otherwise.
 static size_t split_workspace(int64_t M, int64_t N, int64_t K) {
@@ -251,10 +260,45 @@ static size_t wide_workspace(int64_t M, int64_t K) {
   return round256((size_t)wide_rows(M) * (size_t)K);
 }
 
-// mq_fused_gemm's workspace: the wide activation codes, then the split-K
-// partials.
-static size_t gemm_workspace(int64_t M, int64_t N, int64_t K) {
+// mq_fused_gemm's workspace on the int8 route: the wide activation codes,
+// then the split-K partials.
+static size_t gemm_workspace_i8(int64_t M, int64_t N, int64_t K) {
   return wide_workspace(M, K) + split_workspace(M, N, K);
+}
+
+// The fp6 route (M > 32, block 64 or 128): FP6 images of the activation
+// codes, the base weights and the residual blocks, then the split-K
+// partials.  fp6_images_bytes is exact for (block, n_select); with
+// n_select unknown the residual term is bounded by N*K*3/4 (every block
+// selected).
+static size_t fp6_images_bytes(int64_t M, int64_t N, int64_t K, int block, int64_t n_select) {
+  return round256(fp6_rows_bytes(M, K)) + round256(fp6_rows_bytes(N, K)) +
+         round256(fp6_residual_bytes(n_select, block));
+}
+static size_t fp6_images_bound(int64_t M, int64_t N, int64_t K) {
+  if (M <= 32 || N <= 0 || K < kGroup) return 0;
+  return round256(fp6_rows_bytes(M, K)) + round256(fp6_rows_bytes(N, K)) + round256((size_t)N * (size_t)K * 3 / 4);
+}
+static size_t gemm_workspace(int64_t M, int64_t N, int64_t K) {
+  const size_t i8 = gemm_workspace_i8(M, N, K);
+  const size_t f6 = M >= kFp6MinM ? fp6_images_bound(M, N, K) + split_workspace(M, N, K) : 0;
+  return i8 > f6 ? i8 : f6;
+}
+
+// Points a at the fp6 images in ws (layout of fp6_images_bytes) and
+// enqueues the conversions of the weights and the residual blocks.
+static hipError_t fp6_prepare(GemmArgs& a, uint8_t* ws, hipStream_t st) {
+  uint8_t* aimg = ws;
+  uint8_t* wimg = aimg + round256(fp6_rows_bytes(a.M, a.K));
+  uint8_t* rimg = wimg + round256(fp6_rows_bytes(a.N, a.K));
+  hipError_t e = launch_weights_fp6(a.qw, a.N, a.K, wimg, st);
+  if (e != hipSuccess) return e;
+  e = launch_residual_fp6(a.qr, a.n_select, a.block, rimg, st);
+  if (e != hipSuccess) return e;
+  a.aimg = aimg;
+  a.wimg = wimg;
+  a.rimg = rimg;
+  return hipSuccess;
 }
 
 mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes) {
@@ -273,7 +317,10 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
                         size_t workspace_bytes, uint32_t flags, int32_t* acc_dump,
                         void* stream) {
   g_err[0] = 0;
-  MQ_REQUIRE((flags & ~MQ_FLAG_DUMP_ACC) == 0, MQ_ERR_ARG, "unknown flags 0x%x", flags);
+  MQ_REQUIRE((flags & ~(MQ_FLAG_DUMP_ACC | MQ_FLAG_INT8_TILE | MQ_FLAG_FP6_TILE)) == 0, MQ_ERR_ARG,
+             "unknown flags 0x%x", flags);
+  MQ_REQUIRE(!((flags & MQ_FLAG_INT8_TILE) && (flags & MQ_FLAG_FP6_TILE)), MQ_ERR_ARG,
+             "MQ_FLAG_INT8_TILE and MQ_FLAG_FP6_TILE exclude each other");
   MQ_REQUIRE(valid_block(block), MQ_ERR_BLOCK, "block = %d must be 32, 64 or 128", block);
   MQ_REQUIRE(M >= 0, MQ_ERR_SHAPE, "M = %lld must be >= 0", (long long)M);
   MQ_REQUIRE(N > 0 && N % block == 0, MQ_ERR_SHAPE, "N = %lld must be a positive multiple of %d",
@@ -321,15 +368,28 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
   // copied once into the wide fragment order, which the tile kernel moves
   // to LDS without widening, and the split-K schedule is used where it
   // applies.  Otherwise one pass over K from the packed codes.
-  const size_t need = gemm_workspace(M, N, K);
-  const bool wide = need > 0 && workspace && workspace_bytes >= need && M > 32 && tile_gemm_fits(a);
-  if (wide) {
+  const size_t split = split_workspace(M, N, K);
+  const size_t need6 = M > 32 ? fp6_images_bytes(M, N, K, block, n_select) + split : 0;
+  const size_t need = gemm_workspace_i8(M, N, K);
+  const int64_t min_m6 = (flags & MQ_FLAG_FP6_TILE) ? 33 : kFp6MinM;
+  const bool fp6 = !(flags & MQ_FLAG_INT8_TILE) && M >= min_m6 && workspace && workspace_bytes >= need6 &&
+                   tile6_gemm_fits(a);
+  const bool wide = !fp6 && need > 0 && workspace && workspace_bytes >= need && M > 32 && tile_gemm_fits(a);
+  if (fp6) {
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    mq_status st = hip_status(fp6_prepare(a, ws, (hipStream_t)stream), "mq_fused_gemm fp6 conversion launch");
+    if (st != MQ_OK) return st;
+    st = hip_status(launch_acts_fp6(qa, M, K, const_cast<uint8_t*>(a.aimg), (hipStream_t)stream),
+                    "mq_fused_gemm fp6 conversion launch");
+    if (st != MQ_OK) return st;
+    a.part = split > 0 ? reinterpret_cast<float*>(ws + need6 - split) : nullptr;
+    a.ksplit = split > 0 ? tile_gemm_splits(M, N, K) : 1;
+  } else if (wide) {
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const mq_status st = hip_status(launch_widen_acts(qa, M, K, ws, (hipStream_t)stream),
                                     "mq_fused_gemm widen launch");
     if (st != MQ_OK) return st;
     a.qaw = ws;
-    const size_t split = split_workspace(M, N, K);
     a.part = split > 0 ? reinterpret_cast<float*>(ws + wide_workspace(M, K)) : nullptr;
     a.ksplit = split > 0 ? tile_gemm_splits(M, N, K) : 1;
   } else {
@@ -346,9 +406,20 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
 static size_t layer_codes_bytes(int64_t M, int64_t K) {
   return M > 32 ? wide_workspace(M, K) : round256((size_t)tiled_rows(M) * (size_t)(K / 2));
 }
-static size_t layer_workspace(int64_t M, int64_t N, int64_t K) {
+static size_t layer_workspace_i8(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < kGroup || stream_quant_fits(M, N, K)) return 0;
   return layer_codes_bytes(M, K) + round256((size_t)M * (size_t)(K / kGroup) * 4) + split_workspace(M, N, K);
+}
+// The fp6 route: the activation scales, the fp6 images, the split-K partials.
+static size_t layer_scales_bytes(int64_t M, int64_t K) { return round256((size_t)M * (size_t)(K / kGroup) * 4); }
+static size_t layer_workspace_fp6(int64_t M, int64_t N, int64_t K, int block, int64_t n_select) {
+  return layer_scales_bytes(M, K) + fp6_images_bytes(M, N, K, block, n_select) + split_workspace(M, N, K);
+}
+static size_t layer_workspace(int64_t M, int64_t N, int64_t K) {
+  const size_t i8 = layer_workspace_i8(M, N, K);
+  if (M < kFp6MinM || N <= 0 || K < kGroup) return i8;
+  const size_t f6 = layer_scales_bytes(M, K) + fp6_images_bound(M, N, K) + split_workspace(M, N, K);
+  return i8 > f6 ? i8 : f6;
 }
 
 mq_status mq_fused_layer_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes) {
@@ -403,19 +474,21 @@ static mq_status layer_check(const uint16_t* x, int64_t M, int64_t K, int64_t ld
                  aligned16(row_ptr) && aligned16(col_idx) && aligned16(qr) && aligned16(sr) &&
                  aligned16(workspace),
              MQ_ERR_ALIGN, "device pointers must be 16-byte aligned");
-  *need = layer_workspace(M, N, K);
+  *need = layer_workspace_i8(M, N, K);
   return MQ_OK;
 }
 
-// Launches of the one-call layer on `ws` (at least layer_workspace's bytes;
-// unused when that is 0): one kernel when the streaming GEMM quantises the
-// activations itself, else act-quant into the workspace, then the fused
-// GEMM with its split-K partials after the codes and scales.
+// Launches of the one-call layer on `ws` of ws_bytes (at least
+// layer_workspace_i8's `need`; unused when that is 0): one kernel when the
+// streaming GEMM quantises the activations itself; for M > 32 with room for
+// the fp6 images, act-quant into the FP6 image, the weight and residual
+// conversions and the fp6 tile kernel; else act-quant into the workspace,
+// then the fused GEMM with its split-K partials after the codes and scales.
 static mq_status layer_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int64_t N,
                            const uint8_t* qw, const uint16_t* sw, int32_t block, int32_t n_select,
                            const int32_t* row_ptr, const int32_t* col_idx, const uint8_t* qr,
                            const uint16_t* sr, uint16_t* y, int64_t ldy, uint8_t* ws, size_t need,
-                           hipStream_t st) {
+                           size_t ws_bytes, hipStream_t st) {
   GemmArgs a = {};
   a.M = M;
   a.N = N;
@@ -436,6 +509,23 @@ static mq_status layer_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
     a.ldx = ldx;
     return hip_status(launch_fused_gemm(a, st), "mq_fused_layer launch");
   }
+  const size_t split = split_workspace(M, N, K);
+  if (M >= kFp6MinM && tile6_gemm_fits(a) && ws_bytes >= layer_workspace_fp6(M, N, K, block, n_select)) {
+    // fp6 tile kernel: scales, then the images
+    float* sa6 = reinterpret_cast<float*>(ws);
+    a.sa = sa6;
+    mq_status s = hip_status(fp6_prepare(a, ws + layer_scales_bytes(M, K), st),
+                             "mq_fused_layer fp6 conversion launch");
+    if (s != MQ_OK) return s;
+    s = hip_status(launch_act_quant_fp6(x, M, K, ldx, const_cast<uint8_t*>(a.aimg), sa6, st),
+                   "mq_fused_layer act-quant launch");
+    if (s != MQ_OK) return s;
+    if (split > 0) {
+      a.part = reinterpret_cast<float*>(ws + layer_workspace_fp6(M, N, K, block, n_select) - split);
+      a.ksplit = tile_gemm_splits(M, N, K);
+    }
+    return hip_status(launch_fused_gemm(a, st), "mq_fused_layer launch");
+  }
   float* sa = reinterpret_cast<float*>(ws + layer_codes_bytes(M, K));
   a.sa = sa;
   if (M > 32 && tile_gemm_fits(a)) {
@@ -444,7 +534,6 @@ static mq_status layer_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                                    "mq_fused_layer act-quant launch");
     if (s != MQ_OK) return s;
     a.qaw = ws;
-    const size_t split = split_workspace(M, N, K);
     if (split > 0) {
       a.part = reinterpret_cast<float*>(ws + need - split);
       a.ksplit = tile_gemm_splits(M, N, K);
@@ -513,10 +602,12 @@ mq_status mq_fused_layer(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, i
   mq_status s = layer_check(x, M, K, ldx, N, qw, sw, block, n_select, row_ptr, col_idx, qr, sr, y,
                             ldy, workspace, &empty, &need);
   if (s != MQ_OK || empty) return s;
+  need = layer_workspace(M, N, K);
   MQ_REQUIRE(workspace_bytes >= need && (need == 0 || workspace), MQ_ERR_WORKSPACE,
              "workspace of %zu bytes given, %zu needed", workspace_bytes, need);
   return layer_run(x, M, K, ldx, N, qw, sw, block, n_select, row_ptr, col_idx, qr, sr, y, ldy,
-                   static_cast<uint8_t*>(workspace), need, (hipStream_t)stream);
+                   static_cast<uint8_t*>(workspace), layer_workspace_i8(M, N, K), workspace_bytes,
+                   (hipStream_t)stream);
 }
 
 mq_status mq_fused_layer_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, int64_t N,
@@ -539,7 +630,7 @@ mq_status mq_fused_layer_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_
     if (s != MQ_OK) return s;
   }
   return layer_run(x, M, K, ldx, N, qw, sw, block, n_select, row_ptr, col_idx, qr, sr, y, ldy,
-                   static_cast<uint8_t*>(ws), need, (hipStream_t)stream);
+                   static_cast<uint8_t*>(ws), need, need > 0 ? kScratchBytes : 0, (hipStream_t)stream);
 }
 
 mq_status mq_residual_merge(const uint8_t* qa, const float* sa, int64_t M, int64_t N, int64_t K,
@@ -657,6 +748,113 @@ mq_status mq_validate_csr(const int32_t* row_ptr, const int32_t* col_idx, int64_
     }
   }
   return MQ_OK;
+}
+
+
+// ---- the fp6 route with prepared operands ----
+
+static mq_status fp6_shape(int64_t M, int64_t N, int64_t K, int32_t block, int32_t n_select) {
+  MQ_REQUIRE(block == 64 || block == 128, MQ_ERR_BLOCK, "block = %d: the fp6 route takes 64 or 128", block);
+  MQ_REQUIRE(M >= 0 && M < ((int64_t)1 << 31), MQ_ERR_SHAPE, "M = %lld outside [0, 2^31)", (long long)M);
+  MQ_REQUIRE(N > 0 && N % block == 0 && N < ((int64_t)1 << 31), MQ_ERR_SHAPE,
+             "N = %lld must be a positive multiple of %d below 2^31", (long long)N, block);
+  MQ_REQUIRE(K > 0 && K % kGroup == 0 && K < ((int64_t)1 << 31), MQ_ERR_SHAPE,
+             "K = %lld must be a positive multiple of 128 below 2^31", (long long)K);
+  MQ_REQUIRE(M * K < ((int64_t)1 << 32) && N * K < ((int64_t)1 << 32), MQ_ERR_SHAPE,
+             "M*K and N*K must each be below 2^32");
+  const int64_t B = block_count(N, K, block);
+  MQ_REQUIRE(n_select >= 0 && n_select <= B, MQ_ERR_BUDGET, "n_select = %d outside [0, %lld]", n_select,
+             (long long)B);
+  MQ_REQUIRE((int64_t)n_select * block * block < ((int64_t)1 << 32), MQ_ERR_SHAPE, "residual too large");
+  return MQ_OK;
+}
+
+mq_status mq_fp6_sizes(int64_t M, int64_t N, int64_t K, int32_t block, int32_t n_select, size_t* act_bytes,
+                       size_t* weight_bytes, size_t* split_bytes) {
+  g_err[0] = 0;
+  MQ_REQUIRE(act_bytes && weight_bytes && split_bytes, MQ_ERR_NULL_PTR, "size outputs must be non-NULL");
+  const mq_status s = fp6_shape(M, N, K, block, n_select);
+  if (s != MQ_OK) return s;
+  *act_bytes = fp6_rows_bytes(M, K);
+  *weight_bytes = round256(fp6_rows_bytes(N, K)) + fp6_residual_bytes(n_select, block);
+  *split_bytes = split_workspace(M, N, K);
+  return MQ_OK;
+}
+
+mq_status mq_fp6_prepare_acts(const uint8_t* qa, int64_t M, int64_t K, uint8_t* act_img, void* stream) {
+  g_err[0] = 0;
+  MQ_REQUIRE(M >= 0 && M < ((int64_t)1 << 31) && M * K < ((int64_t)1 << 32), MQ_ERR_SHAPE, "bad M");
+  MQ_REQUIRE(K > 0 && K % kGroup == 0 && K < ((int64_t)1 << 31), MQ_ERR_SHAPE,
+             "K = %lld must be a positive multiple of 128", (long long)K);
+  if (M == 0) return MQ_OK;
+  MQ_REQUIRE(qa && act_img, MQ_ERR_NULL_PTR, "qa and act_img must be non-NULL");
+  MQ_REQUIRE(aligned16(qa) && aligned16(act_img), MQ_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  return hip_status(launch_acts_fp6(qa, M, K, act_img, (hipStream_t)stream), "mq_fp6_prepare_acts launch");
+}
+
+mq_status mq_fp6_prepare_weights(const uint8_t* qw, int64_t N, int64_t K, int32_t block, int32_t n_select,
+                                 const uint8_t* qr, uint8_t* weight_img, void* stream) {
+  g_err[0] = 0;
+  const mq_status s = fp6_shape(0, N, K, block, n_select);
+  if (s != MQ_OK) return s;
+  MQ_REQUIRE(qw && weight_img && (n_select == 0 || qr), MQ_ERR_NULL_PTR,
+             "qw, weight_img (and qr when n_select > 0) must be non-NULL");
+  MQ_REQUIRE(aligned16(qw) && aligned16(qr) && aligned16(weight_img), MQ_ERR_ALIGN,
+             "device pointers must be 16-byte aligned");
+  hipError_t e = launch_weights_fp6(qw, N, K, weight_img, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = launch_residual_fp6(qr, n_select, block, weight_img + round256(fp6_rows_bytes(N, K)), (hipStream_t)stream);
+  return hip_status(e, "mq_fp6_prepare_weights launch");
+}
+
+mq_status mq_fused_gemm_fp6(const uint8_t* act_img, const float* sa, int64_t M, int64_t N, int64_t K,
+                            const uint8_t* weight_img, const uint16_t* sw, int32_t block, int32_t n_select,
+                            const int32_t* row_ptr, const int32_t* col_idx, const uint16_t* sr, uint16_t* y,
+                            int64_t ldy, void* split_ws, size_t split_bytes, uint32_t flags, int32_t* acc_dump,
+                            void* stream) {
+  g_err[0] = 0;
+  MQ_REQUIRE((flags & ~MQ_FLAG_DUMP_ACC) == 0, MQ_ERR_ARG, "unknown flags 0x%x", flags);
+  mq_status s = fp6_shape(M, N, K, block, n_select);
+  if (s != MQ_OK) return s;
+  MQ_REQUIRE(M == 0 || M > 32, MQ_ERR_SHAPE, "M = %lld: the fp6 route takes M > 32", (long long)M);
+  MQ_REQUIRE(ldy >= N && ldy % 8 == 0, MQ_ERR_SHAPE, "ldy = %lld must be >= N and a multiple of 8",
+             (long long)ldy);
+  if (M == 0) return MQ_OK;
+  MQ_REQUIRE(act_img && sa && weight_img && sw && y, MQ_ERR_NULL_PTR,
+             "act_img, sa, weight_img, sw and y must be non-NULL");
+  MQ_REQUIRE(n_select == 0 || (row_ptr && col_idx && sr), MQ_ERR_NULL_PTR,
+             "row_ptr, col_idx and sr must be non-NULL when n_select > 0");
+  MQ_REQUIRE(!(flags & MQ_FLAG_DUMP_ACC) || acc_dump, MQ_ERR_NULL_PTR, "acc_dump must be non-NULL with the flag");
+  MQ_REQUIRE(aligned16(act_img) && aligned16(sa) && aligned16(weight_img) && aligned16(sw) && aligned16(y) &&
+                 aligned16(row_ptr) && aligned16(col_idx) && aligned16(sr) && aligned16(split_ws) &&
+                 aligned16(acc_dump),
+             MQ_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  const size_t split = split_workspace(M, N, K);
+  MQ_REQUIRE(split == 0 || (split_ws && split_bytes >= split), MQ_ERR_WORKSPACE,
+             "split-K workspace of %zu bytes given, %zu needed", split_bytes, split);
+  GemmArgs a = {};
+  a.sa = sa;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.qw = nullptr;
+  a.sw = sw;
+  a.block = block;
+  a.n_select = n_select;
+  a.row_ptr = n_select ? row_ptr : nullptr;
+  a.col_idx = n_select ? col_idx : nullptr;
+  a.sr = n_select ? sr : nullptr;
+  a.y = y;
+  a.ldy = ldy;
+  a.acc_dump = (flags & MQ_FLAG_DUMP_ACC) ? acc_dump : nullptr;
+  a.aimg = act_img;
+  a.wimg = weight_img;
+  a.rimg = weight_img + round256(fp6_rows_bytes(N, K));
+  MQ_REQUIRE(tile6_gemm_fits(a), MQ_ERR_SHAPE, "K = %lld too long for the fp6 kernel's residual table",
+             (long long)K);
+  a.part = split > 0 ? static_cast<float*>(split_ws) : nullptr;
+  a.ksplit = split > 0 ? tile_gemm_splits(M, N, K) : 1;
+  return hip_status(launch_tile6_gemm(a, (hipStream_t)stream), "mq_fused_gemm_fp6 launch");
 }
 
 }  // extern "C"

@@ -616,6 +616,7 @@ hipError_t launch_fused_gemm(const GemmArgs& a, hipStream_t st) {
   // kernel (weights read once per 256-token tile); small M, or a K too long
   // for the tile kernel's LDS table: the streaming kernel (weights read once
   // per 16-token tile)
+  if (!a.x && a.aimg) return launch_tile6_gemm(a, st);
   if (!a.x && a.M > 32 && tile_gemm_fits(a)) return launch_tile_gemm(a, st);
   switch (a.block) {
     case 32: return launch_blk<32>(a, st);

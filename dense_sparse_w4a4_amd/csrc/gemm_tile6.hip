@@ -1,0 +1,505 @@
+// ZipperEngine fused layer for large M (prefill), fp6 route: the LDS-tiled
+// GEMM of gemm_tile.hip with its operands on the FP6 matrix core.
+// MosaicQuant technical summary (gist.science/pt/paper/2606.15652),
+// Metodologia 3: one kernel runs the dense 4-bit GEMM, the sparse residual
+// compensation and the scale/reduce-sum epilogue, the residual reusing the
+// activation tile of the dense product.
+//
+// The 4-bit codes reach this kernel re-encoded as FP6 E2M3 images (fp6.hip,
+// layout in mq_internal.h): each field's value is exactly q/8, so one
+// V_MFMA_F32_32X32X64_F8F6F4 gives the exact integer dot product of 64
+// codes / 64, in fp32.  On gfx950 that instruction takes as long as one
+// V_MFMA_I32_32X32X32_I8 for twice the K, and its fp32 result needs no
+// conversion before the per-group scaling: per 32 x 32 sub-tile and group
+// two FP6 MFMAs, one scale-product MFMA and 16 FMAs per lane, where the int8
+// route has four int8 MFMAs, one scale-product MFMA, 16 converts and 16 FMAs.
+//
+// Tile: 256 tokens x 128 output channels per workgroup of eight waves (wave
+// w computes the 64 x 64 quarter (w % 4, w / 4), four 32 x 32 sub-tiles).
+// Per 128-channel group the workgroup's LDS stage holds
+//   A  eight 32-token row blocks' images (24 KB), copied from memory by LDS
+//      DMA (wave w: row block w, three 1 KB pieces);
+//   B  four 32-channel column blocks' weight images (12 KB), by LDS DMA
+//      (pieces w and w + 8 of the twelve);
+//   R  the residual images of the tile's selected blocks in this group, in
+//      the column blocks' layout (12 KB; wave w stages column block w / 2,
+//      slice w % 2 through registers; rows of unselected blocks hold unused
+//      data);
+//   the scale operands: per token sa * 64 and per channel sw (and the
+//      residual row scales) as (hi, lo) bf16 pairs; one
+//      V_MFMA_F32_32X32X8_BF16 forms each sub-tile's 32 x 32 products
+//      sa * sw (exact in sw, within 2^-16 in sa), and the factor 64 undoes
+//      the fields' 1/8 on both operands.
+// Every product S * D equals the int8 route's (both are sa * sw * dot up to
+// the same bf16 split, scaled by powers of two), so the two routes give the
+// same fp32 partial sums and the same fp16 outputs.
+//
+// Pipeline, residual table, split-K and work order as in gemm_tile.hip: two
+// LDS stages, one LDS-only barrier per group, register buffers two groups
+// ahead, every step issuing the same loads (dummy offsets where no residual
+// block is selected) so that the DMA wait counts them exactly.
+#include "gemm_common.h"
+
+namespace mq {
+namespace {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+constexpr int TBM = 256;
+constexpr int TBN = 128;
+constexpr int NTHR = 512;
+constexpr size_t kMaxLds = 160 * 1024;
+
+template <int BLK>
+struct Tile6Cfg {
+  static constexpr int NBR = TBN / BLK;      // block rows in a tile
+  static constexpr int NBC = kGroup / BLK;   // block columns in a group
+  static constexpr int NS = BLK / 64;        // 64-code slices of a block
+  static constexpr int NSRS = TBN * NBC;     // residual-scale slots (<= NTHR)
+  static constexpr int A_OFF = 0;                     // 8 row blocks x 3 KB
+  static constexpr int B_OFF = 8 * kFp6Frag;          // 4 column blocks x 3 KB
+  static constexpr int R_OFF = B_OFF + 4 * kFp6Frag;  // 4 column blocks x 3 KB
+  static constexpr int SA_OFF = R_OFF + 4 * kFp6Frag; // [8 row blocks][32 lanes] x 8 bytes
+  static constexpr int SW_OFF = SA_OFF + 8 * 256;     // [4 column blocks][32 lanes] x 8 bytes
+  static constexpr int SR_OFF = SW_OFF + 4 * 256;     // [4 column blocks][NBC][32 lanes] x 8 bytes
+  static constexpr int STAGE = SR_OFF + 4 * NBC * 256;
+  static constexpr int ZERO_OFF = 2 * STAGE;          // 16 zero bytes
+  static constexpr int TAB_OFF = ZERO_OFF + 16;
+  static size_t lds(int64_t K) {
+    return (size_t)TAB_OFF + (size_t)NBR * (size_t)(K / BLK) * 2 + (size_t)(K / kGroup);
+  }
+};
+
+typedef __attribute__((address_space(3))) v4i lds_v4i;
+typedef __attribute__((address_space(3))) v4s lds_v4s;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) u32x2 lds_u2;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ v4i lds_ld16(uint32_t a) { return *(const lds_v4i*)(uintptr_t)a; }
+__device__ __forceinline__ v4s lds_ld8(uint32_t a) { return *(const lds_v4s*)(uintptr_t)a; }
+__device__ __forceinline__ u32x2 lds_ld8u(uint32_t a) { return *(const lds_u2*)(uintptr_t)a; }
+__device__ __forceinline__ void lds_st16(uint32_t a, v4i v) { *(lds_v4i*)(uintptr_t)a = v; }
+__device__ __forceinline__ void lds_st8(uint32_t a, uint32_t lo, uint32_t hi) {
+  const u32x2 v = {lo, hi};
+  *(lds_u2*)(uintptr_t)a = v;
+}
+
+// This wave's LDS writes complete, then s_barrier (the global loads of later
+// groups stay in flight; LDS DMA is waited for separately, before it).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// One lane's FP6 operand: its dwords 0-3 at LDS address lo, 4-5 at hi.
+// Callers pass bases that already hold the lane's offsets (fp6_lo_offset /
+// fp6_hi_offset at u = 0) plus compile-time offsets of the fragment, which
+// fold into the instructions' offset fields.
+__device__ __forceinline__ v8i frag6(uint32_t lo_a, uint32_t hi_a) {
+  const v4i lo = lds_ld16(lo_a);
+  const u32x2 hi = lds_ld8u(hi_a);
+  const v8i r = {lo[0], lo[1], lo[2], lo[3], (int)hi[0], (int)hi[1], 0, 0};
+  return r;
+}
+// D = A . B + C on FP6 E2M3 operands (format code 2 for both).
+__device__ __forceinline__ v16f mfma6(v8i a, v8i b, v16f c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 2, 2, 0, 0, 0, 0);
+}
+__device__ __forceinline__ v16f mfma_scale(v4s a, v4s b) {
+  const v16f z = {};
+  return __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, z, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+__device__ __forceinline__ float bf16_value(uint32_t b) { return __uint_as_float(b << 16); }
+// (hi, lo) bf16 pair with hi + lo = x to within 2^-16 relative (exactly for
+// an fp16 x).
+__device__ __forceinline__ uint32_t split_bf16(float x) {
+  const uint32_t hi = bf16_bits(x);
+  const uint32_t lo = bf16_bits(x - bf16_value(hi));
+  return hi | (lo << 16);
+}
+
+struct Stage6 {
+  v4i Rlo;
+  u32x2 Rhi;
+  uint32_t sc;  // activation scale bits (waves 0-3) or weight scale bits (waves 4-5)
+  uint32_t sr;  // residual row scale bits
+};
+
+template <int BLK, bool DUMP>
+__global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
+  using C = Tile6Cfg<BLK>;
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int G = (int)(a.K / kGroup);
+  const int KT = (int)(a.K / BLK);
+  uint16_t* tab = reinterpret_cast<uint16_t*>(smem + C::TAB_OFF);  // [NBR][KT]: entry-rp+1, 0 = none
+  uint8_t* anyr = smem + C::TAB_OFF + C::NBR * KT * 2;              // [G]: a selected block in group j
+  __shared__ int rp_row[C::NBR];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;
+  const int lane = tid & 63;
+
+  // work order: XCD-aware, banded, split-K as in the int8 route
+  const int tiles_n = (int)((a.N + TBN - 1) / TBN);
+  const int items = (int)gridDim.x;
+  const int tiles = items / a.ksplit;
+  const int xcd = blockIdx.x % 8;
+  const int per = items / 8, rem = items % 8;
+  const int item = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + blockIdx.x / 8;
+  const int split = item / tiles;
+  const int tile = item - split * tiles;
+  const int jb = (int)((int64_t)split * G / a.ksplit);
+  const int je = (int)((int64_t)(split + 1) * G / a.ksplit);
+  constexpr int kBand = 4;
+  const int tiles_m = tiles / tiles_n;
+  const int band = tile / (kBand * tiles_n);
+  const int bh = min(kBand, tiles_m - band * kBand);
+  const int rbi = tile - band * kBand * tiles_n;
+  const int64_t m0 = (int64_t)(band * kBand + rbi % bh) * TBM;
+  const int64_t n0 = (int64_t)(rbi / bh) * TBN;
+  const int nt0 = (int)(n0 / BLK);
+  const int nrows_b = (int)(a.N / BLK);
+
+  // ---- entry table of the tile's block rows: tab[rb][kt]; anyr[j] ----
+  for (int i = tid; i < C::NBR * KT; i += NTHR) tab[i] = 0;
+  for (int i = tid; i < G; i += NTHR) anyr[i] = 0;
+  if (tid < 4) reinterpret_cast<uint32_t*>(smem + C::ZERO_OFF)[tid] = 0u;
+  if (tid < C::NBR) {
+    int r0 = 0;
+    if (a.n_select > 0 && nt0 + tid < nrows_b) r0 = min(max(a.row_ptr[nt0 + tid], 0), a.n_select);
+    rp_row[tid] = r0;
+  }
+  __syncthreads();
+  if (a.n_select > 0) {
+#pragma unroll
+    for (int rb = 0; rb < C::NBR; ++rb) {
+      if (nt0 + rb >= nrows_b) break;
+      const int b0 = rp_row[rb];
+      const int b1 = min(max(a.row_ptr[nt0 + rb + 1], b0), a.n_select);
+      for (int e = b0 + tid; e < b1 && e - b0 < 0xFFFF; e += NTHR) {
+        const int kt = a.col_idx[e];
+        if (kt >= 0 && kt < KT) {
+          tab[rb * KT + kt] = (uint16_t)(e - b0 + 1);
+          anyr[kt / C::NBC] = 1;  // (benign race: every writer stores 1)
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- operand copies by LDS DMA ----
+  // A: wave w copies row block w of the tile (row blocks past the last one
+  // of M re-read the last one).  B: wave w copies pieces w and, for w < 4,
+  // w + 8 of the twelve 1 KB pieces (column block p / 3, piece p % 3) of the
+  // four column blocks (past N: the last one).
+  const int64_t nrb = wide_rows(a.M) / 32;
+  const int64_t ncb = a.N / 32;
+  const uint8_t* srcA = a.aimg + min(m0 / 32 + wave, nrb - 1) * G * kFp6Frag + lane * 16;
+  const int pB0 = wave, pB1 = wave + 8;
+  const uint8_t* srcB0 = a.wimg + min(n0 / 32 + pB0 / 3, ncb - 1) * G * kFp6Frag + (pB0 % 3) * 1024 + lane * 16;
+  const uint8_t* srcB1 =
+      a.wimg + min(n0 / 32 + (pB1 < 12 ? pB1 : 0) / 3, ncb - 1) * G * kFp6Frag + (pB1 % 3) * 1024 + lane * 16;
+  const uint32_t dstB0 = (uint32_t)(C::B_OFF + (pB0 / 3) * kFp6Frag + (pB0 % 3) * 1024);
+  const uint32_t dstB1 = (uint32_t)(C::B_OFF + ((pB1 < 12 ? pB1 : 0) / 3) * kFp6Frag + (pB1 % 3) * 1024);
+  typedef __attribute__((address_space(3))) void* lds_ptr;
+  auto dma = [&](uint32_t st, int j) {
+    j = min(j, je - 1);
+    const int64_t jo = (int64_t)j * kFp6Frag;
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+      __builtin_amdgcn_global_load_lds(srcA + jo + p * 1024,
+                                       (lds_ptr)(uintptr_t)(st + C::A_OFF + (uint32_t)wave * kFp6Frag + p * 1024), 16,
+                                       0, 0);
+    __builtin_amdgcn_global_load_lds(srcB0 + jo, (lds_ptr)(uintptr_t)(st + dstB0), 16, 0, 0);
+    if (wave < 4) __builtin_amdgcn_global_load_lds(srcB1 + jo, (lds_ptr)(uintptr_t)(st + dstB1), 16, 0, 0);
+  };
+  // after a step's loads: the step's DMA (issued before the step's four
+  // register loads: scale, residual pieces, residual scale) has completed
+  auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
+
+  // ---- register staging: scales, residual pieces ----
+  // Residual: wave w stages column block cbw = w / 2, slice uw = w % 2 of
+  // the tile's selected block there (block row cbw*32/BLK, block column
+  // uw*64/BLK of the group; its piece (cbw*32 % BLK)/32 * NS + (uw*64 % BLK)/64).
+  const uint8_t* rbase = a.n_select > 0 ? a.rimg : a.wimg;
+  const uint8_t* sbase = a.n_select > 0 ? reinterpret_cast<const uint8_t*>(a.sr)
+                                        : reinterpret_cast<const uint8_t*>(a.sw);
+  const int cbw = wave >> 1, uw = wave & 1;
+  const int rbtw = (cbw * 32) / BLK;
+  const int tabR = rbtw * KT + (uw * 64) / BLK;  // (rows past N: table zero, dummy loads)
+  const int64_t rblk = (int64_t)BLK * BLK * 3 / 4;
+  const int64_t roff = (int64_t)((((cbw * 32) % BLK) / 32) * C::NS + ((uw * 64) % BLK) / 64) * 1536;
+  const int rrp = rp_row[rbtw] - 1;
+  const uint32_t dstRlo = (uint32_t)(C::R_OFF + cbw * kFp6Frag + fp6_lo_offset(uw, lane));
+  const uint32_t dstRhi = (uint32_t)(C::R_OFF + cbw * kFp6Frag + fp6_hi_offset(uw, lane));
+  int tabS, baseS;
+  uint32_t slotS;
+  {
+    // residual scale slot tid: channel r = tid / NBC, block column c = tid % NBC
+    const int r = min(tid / C::NBC, TBN - 1), c = tid % C::NBC;
+    const int64_t n = min(n0 + r, a.N - 1);
+    const int rb = (int)(n / BLK) - nt0;
+    tabS = tid < C::NSRS ? rb * KT + c : -1;
+    baseS = ((rp_row[rb] - 1) * BLK + (int)(n - (int64_t)(nt0 + rb) * BLK)) * 2;
+    slotS = (uint32_t)(C::SR_OFF + (((r >> 5) * C::NBC + c) * 32 + (r & 31)) * 8);
+  }
+  const uint32_t offS = wave < 4 ? (uint32_t)(min(m0 + tid, a.M - 1) * G * 4)
+                                 : (uint32_t)(min(n0 + min(tid - 256, TBN - 1), a.N - 1) * G * 2);
+
+  auto load = [&](Stage6& S, int j) {
+    j = min(j, je - 1);
+    if (wave < 4) {
+      S.sc = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.sa) + j * 4 + offS);
+    } else {
+      S.sc = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.sw) + j * 2 + offS);
+    }
+    // residual pieces and row scales: loaded in every step, from offset 0 of
+    // a valid buffer where no block is selected, so the DMA wait is exact
+    const int entR = (int)tab[tabR + j * C::NBC];
+    const int entS = (int)tab[max(tabS, 0) + j * C::NBC];
+    const uint8_t* rp = rbase + (entR > 0 ? (int64_t)(rrp + entR) * rblk + roff : 0);
+    S.Rlo = *reinterpret_cast<const v4i*>(rp + lane * 16);
+    S.Rhi = *reinterpret_cast<const u32x2*>(rp + 1024 + lane * 8);
+    const int es = tabS >= 0 ? entS : 0;
+    S.sr = *reinterpret_cast<const uint16_t*>(sbase + (uint32_t)(es > 0 ? es * (BLK * 2) + baseS : 0));
+  };
+
+  auto store = [&](uint32_t st, const Stage6& S, int j) {
+    if (wave < 4) {
+      // activation scale * 64 (the fields' 1/8 on both operands): (hi, lo, hi, lo)
+      const float s = (m0 + tid < a.M) ? __uint_as_float(S.sc) * 64.0f : 0.f;
+      const uint32_t p = split_bf16(s);
+      lds_st8(st + C::SA_OFF + (uint32_t)tid * 8, p, p);
+    } else if (wave < 6) {
+      // weight scale: (hi, hi, lo, lo)
+      const uint32_t p = split_bf16(h2f((uint16_t)S.sc));
+      const uint32_t hi = p & 0xFFFFu, lo = p >> 16;
+      lds_st8(st + C::SW_OFF + (uint32_t)(tid - 256) * 8, hi | (hi << 16), lo | (lo << 16));
+    }
+    if (anyr[j]) {
+      lds_st16(st + dstRlo, S.Rlo);
+      lds_st8(st + dstRhi, S.Rhi[0], S.Rhi[1]);
+      if (tid < C::NSRS) {
+        const uint32_t p = split_bf16(h2f((uint16_t)S.sr));
+        const uint32_t hi = p & 0xFFFFu, lo = p >> 16;
+        lds_st8(st + slotS, hi | (hi << 16), lo | (lo << 16));
+      }
+    }
+  };
+
+  const int wm = wave & 3, wn = wave >> 2;
+  float y[2][2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) y[i][q][e] = 0.f;
+  const v16f zero16 = {};
+
+  auto epi = [](float (&yt)[16], const v16f& S, const v16f& d) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) yt[e] = fmaf(S[e], d[e], yt[e]);
+  };
+
+  // residual-table lookups of this wave for group j: lane q*NBC + c holds
+  // the entry of the wave's column block q, block column c (0 = none)
+  const int tq = min(lane / C::NBC, 1), tc = lane % C::NBC;
+  const int tnt = (int)((n0 + (wn * 2 + tq) * 32) / BLK);
+  const bool tvalid = lane < 2 * C::NBC && tnt < nrows_b;
+  const int tidx = tvalid ? (tnt - nt0) * KT + tc : 0;
+  const uint32_t zaddr = lds_addr(smem) + C::ZERO_OFF;
+
+  auto compute = [&](uint32_t st, int j) {
+    // lane bases of the wave's row / column blocks (and of its residual
+    // column blocks), recomputed from opaque copies in every step so that
+    // only compile-time constants remain in the fragment addresses
+    uint32_t la = st + C::A_OFF + (uint32_t)wm * (2 * kFp6Frag) + (uint32_t)lane * 16u;
+    uint32_t ha = st + C::A_OFF + (uint32_t)wm * (2 * kFp6Frag) + 2048u + (uint32_t)lane * 8u;
+    uint32_t lb = st + C::B_OFF + (uint32_t)wn * (2 * kFp6Frag) + (uint32_t)lane * 16u;
+    uint32_t hb = st + C::B_OFF + (uint32_t)wn * (2 * kFp6Frag) + 2048u + (uint32_t)lane * 8u;
+    uint32_t sa_b = lane < 32 ? st + C::SA_OFF + (uint32_t)lane * 8u + (uint32_t)wm * 512u : zaddr;
+    uint32_t sw_b = lane < 32 ? st + C::SW_OFF + (uint32_t)lane * 8u + (uint32_t)wn * 512u : zaddr;
+    const uint32_t sstep = lane < 32 ? 256u : 0u;
+    asm volatile("" : "+v"(la), "+v"(ha), "+v"(lb), "+v"(hb), "+v"(sa_b), "+v"(sw_b));
+    int ent_raw = (int)tab[tidx + j * C::NBC];
+    v8i B[2][2], A[2];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+      for (int u = 0; u < 2; ++u) B[cb][u] = frag6(lb + cb * kFp6Frag + u * 1024, hb + cb * kFp6Frag + u * 512);
+    const v4s sa0 = lds_ld8(sa_b), sw0 = lds_ld8(sw_b);
+    const v4s sw1 = lds_ld8(sw_b + sstep), sa1 = lds_ld8(sa_b + sstep);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) A[u] = frag6(la + rb * kFp6Frag + u * 1024, ha + rb * kFp6Frag + u * 512);
+#pragma unroll
+      for (int cb = 0; cb < 2; ++cb) {
+        const v16f S = mfma_scale(rb ? sa1 : sa0, cb ? sw1 : sw0);
+        v16f d = mfma6(A[0], B[cb][0], zero16);
+        d = mfma6(A[1], B[cb][1], d);
+        epi(y[rb][cb], S, d);
+        if (DUMP) {
+          const int64_t n = n0 + (wn * 2 + cb) * 32 + (lane & 31);
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t m = m0 + (wm * 2 + rb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+            if (m < a.M && n < a.N) a.acc_dump[(m * a.N + n) * G + j] = (int)(d[e] * 64.0f);
+          }
+        }
+      }
+    }
+
+    // zipper: residual blocks of the wave's column blocks in group j, against
+    // the same activation images
+    asm volatile("" : "+v"(ent_raw));
+    const int ent_l = tvalid ? ent_raw : 0;
+    const uint64_t pres = __builtin_amdgcn_ballot_w64(ent_l > 0);
+    if (pres) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        if (!((pres >> (q * C::NBC)) & ((1u << C::NBC) - 1u))) continue;
+        const int cbg = wn * 2 + q;
+        const int nt = (int)((n0 + cbg * 32) / BLK);
+        const int rb_t = nt - nt0;
+#pragma unroll
+        for (int c = 0; c < C::NBC; ++c) {
+          if (!((pres >> (q * C::NBC + c)) & 1u)) continue;
+          // (rare path: the residual bases are formed here)
+          const uint32_t lr = st + C::R_OFF + (uint32_t)cbg * kFp6Frag + (uint32_t)lane * 16u;
+          const uint32_t hr = st + C::R_OFF + (uint32_t)cbg * kFp6Frag + 2048u + (uint32_t)lane * 8u;
+          v8i Rf[C::NS];
+#pragma unroll
+          for (int s = 0; s < C::NS; ++s) Rf[s] = frag6(lr + (c * C::NS + s) * 1024, hr + (c * C::NS + s) * 512);
+          const uint32_t sr_a = lane < 32 ? st + C::SR_OFF + (uint32_t)((cbg * C::NBC + c) * 256 + lane * 8) : zaddr;
+          const v4s srq = lds_ld8(sr_a);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) {
+            v16f d = zero16;
+#pragma unroll
+            for (int s = 0; s < C::NS; ++s)
+              d = mfma6(frag6(la + rb * kFp6Frag + (c * C::NS + s) * 1024, ha + rb * kFp6Frag + (c * C::NS + s) * 512),
+                        Rf[s], d);
+            const v16f SR = mfma_scale(rb ? sa1 : sa0, srq);
+            epi(y[rb][q], SR, d);
+            if (DUMP) {
+              const int ent = __builtin_amdgcn_readlane(ent_l, q * C::NBC + c);
+              const int64_t e_g = rp_row[rb_t] + ent - 1;
+              const int rr = (int)(n0 + cbg * 32 + (lane & 31) - (int64_t)nt * BLK);
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                const int64_t m = m0 + (wm * 2 + rb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                if (m < a.M) a.acc_dump[a.M * a.N * G + (e_g * a.M + m) * BLK + rr] = (int)(d[e] * 64.0f);
+              }
+            }
+          }
+        }
+      }
+    }
+  };
+
+  // Two LDS stages, one barrier per group; register buffers R0/R1 hold the
+  // scales and residual pieces of groups j+2 and j+3 in flight.
+  const uint32_t st0 = lds_addr(smem);
+  const uint32_t st1 = st0 + C::STAGE;
+  Stage6 R0, R1;
+  dma(st0, jb);
+  load(R0, jb);
+  load(R1, jb + 1);
+  store(st0, R0, jb);
+  load(R0, jb + 2);
+  dma_wait();
+  lds_barrier();
+  int j = jb;
+  for (; j + 1 < je; j += 2) {
+    dma(st1, j + 1);
+    compute(st0, j);
+    store(st1, R1, min(j + 1, je - 1));
+    load(R1, j + 3);
+    dma_wait();
+    lds_barrier();
+    dma(st0, j + 2);
+    compute(st1, j + 1);
+    store(st0, R0, min(j + 2, je - 1));
+    load(R0, j + 4);
+    dma_wait();
+    lds_barrier();
+  }
+  if (j < je) compute(st0, j);  // odd group count: the last group
+
+  // ---- output ----
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
+      const int64_t n = n0 + (wn * 2 + cb) * 32 + (lane & 31);
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t m = m0 + (wm * 2 + rb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        if (m < a.M && n < a.N) {
+          if (a.part)
+            a.part[((int64_t)split * a.M + m) * a.N + n] = y[rb][cb][e];
+          else
+            a.y[m * a.ldy + n] = f2h_bits(y[rb][cb][e]);
+        }
+      }
+    }
+}
+
+// Split-K reduce: y = fp16(sum of the splits' fp32 partials, in split order).
+__global__ __launch_bounds__(256) void split_reduce6_kernel(const float* __restrict__ part, int ksplit, int64_t M,
+                                                            int64_t N, uint16_t* y, int64_t ldy) {
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= M * N) return;
+  const int64_t m = idx / N, n = idx - m * N;
+  float s = 0.f;
+  for (int k = 0; k < ksplit; ++k) s += part[((int64_t)k * M + m) * N + n];
+  y[m * ldy + n] = f2h_bits(s);
+}
+
+template <int BLK, bool DUMP>
+hipError_t launch_tile6_cfg(const GemmArgs& a, hipStream_t st) {
+  using C = Tile6Cfg<BLK>;
+  const size_t lds = C::lds(a.K);
+  auto kern = gemm_tile6_kernel<BLK, DUMP>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t tiles = ((a.M + TBM - 1) / TBM) * ((a.N + TBN - 1) / TBN);
+  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * a.ksplit)), dim3(NTHR), lds, st, a);
+  e = hipGetLastError();
+  if (e != hipSuccess || a.ksplit == 1) return e;
+  hipLaunchKernelGGL(split_reduce6_kernel, dim3((unsigned)((a.M * a.N + 255) / 256)), dim3(256), 0, st, a.part,
+                     a.ksplit, a.M, a.N, a.y, a.ldy);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// The fp6 route covers blocks of 64 and 128 (a block of 32 is half a 64-code
+// slice, whose other half would belong to another block) and K whose
+// residual table fits in LDS.
+bool tile6_gemm_fits(const GemmArgs& a) {
+  if (a.block != 64 && a.block != 128) return false;
+  if (a.M <= 32 || a.N % 32 != 0) return false;
+  const int64_t lim = (int64_t)1 << 32;
+  if (a.M * a.K >= lim || a.N * a.K >= lim || (int64_t)a.n_select * a.block * a.block >= lim) return false;
+  return a.block == 64 ? Tile6Cfg<64>::lds(a.K) <= kMaxLds : Tile6Cfg<128>::lds(a.K) <= kMaxLds;
+}
+
+hipError_t launch_tile6_gemm(const GemmArgs& a, hipStream_t st) {
+  const bool d = a.acc_dump != nullptr;
+  if (a.block == 64) return d ? launch_tile6_cfg<64, true>(a, st) : launch_tile6_cfg<64, false>(a, st);
+  return d ? launch_tile6_cfg<128, true>(a, st) : launch_tile6_cfg<128, false>(a, st);
+}
+
+}  // namespace mq

@@ -97,6 +97,54 @@ __host__ __device__ inline int64_t wide_a_index(int64_t m, int64_t j, int64_t G,
   return (((m >> 5) * G + j) * 4 + t) * 1024 + ((m & 31) + 32 * h) * 16;
 }
 
+// FP6 operand images of the prefill tile kernel's fp6 route.  The 4-bit
+// codes go to the matrix core as FP6 E2M3 fields in sign-magnitude: the
+// field of q is |q| (<= 8) with the sign in bit 5.  E2M3 with an exponent
+// field of 0 or 1 is linear in its low five bits (n/8 for n <= 15), so the
+// field's value is exactly q/8, every product q_a*q_w/64 and every sum of
+// them is exact in fp32, and V_MFMA_F32_32X32X64_F8F6F4 returns the exact
+// integer dot product / 64 at twice the int8 instruction's K per cycle.
+//
+// Layout: a 32-row block (tokens or output channels) and one group of 128
+// codes take 3 KB, the images of the two 32x32x64 operands (k slices
+// u = 0, 1 of 64 codes).  Lane l = r + 32h (row r, half h) holds the codes
+// 64u + 32h + i, i = 0..31, as fields at bits 6i of six dwords: dwords 0-3
+// at [u * 1024 + 16 l], dwords 4-5 at [2048 + u * 512 + 8 l].  The image of
+// a row block's group is copied to LDS as it is (three 1 KB pieces).
+constexpr int kFp6Frag = 3072;
+
+// Eight packed two's-complement codes (low nibble first) -> eight fields,
+// field i at bits 6i .. 6i+5 of the result.
+__device__ __forceinline__ uint64_t fp6_fields8(uint32_t w) {
+  const uint32_t s = w & 0x88888888u;           // sign bit of each code
+  const uint32_t t = s >> 3;                    // 1 in each negative code
+  const uint32_t m = (w ^ ((s - t) + s)) + t;   // |q| in each nibble (no carries: |q| <= 8)
+  uint64_t r = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t f = ((m >> (4 * i)) & 0xFu) | (((t >> (4 * i)) & 1u) << 5);
+    r |= (uint64_t)f << (6 * i);
+  }
+  return r;
+}
+
+// 32 codes (four words, code i in nibble i % 8 of word i / 8) -> the six
+// operand dwords of one lane.
+__device__ __forceinline__ void fp6_fields32(const uint32_t w[4], uint32_t d[6]) {
+  const uint64_t a = fp6_fields8(w[0]), b = fp6_fields8(w[1]);
+  const uint64_t c = fp6_fields8(w[2]), e = fp6_fields8(w[3]);
+  d[0] = (uint32_t)a;
+  d[1] = (uint32_t)(a >> 32) | (uint32_t)(b << 16);
+  d[2] = (uint32_t)(b >> 16);
+  d[3] = (uint32_t)c;
+  d[4] = (uint32_t)(c >> 32) | (uint32_t)(e << 16);
+  d[5] = (uint32_t)(e >> 16);
+}
+
+// Byte offsets of a lane's two pieces within a 3 KB row-block group image.
+__host__ __device__ constexpr int fp6_lo_offset(int u, int l) { return u * 1024 + 16 * l; }
+__host__ __device__ constexpr int fp6_hi_offset(int u, int l) { return 2048 + u * 512 + 8 * l; }
+
 // Eight fp16 values held in a uint4 -> floats.
 __device__ __forceinline__ void unpack_h8(const uint4& v, float f[8]) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -178,6 +226,12 @@ struct GemmArgs {
                       // (packed qa, widened while staged)
   const uint8_t* qat; // streaming kernel: packed activation codes in 16-token
                       // tiles (tiled_a_index), or null (qa row-major)
+  // fp6 route of the tile kernel (all three set, or none): FP6 images of the
+  // activation codes [ceil(M/32)][K/128][3 KB], the base weight codes
+  // [N/32][K/128][3 KB] and the residual blocks [n_select][b*b*3/4]
+  const uint8_t* aimg;
+  const uint8_t* wimg;
+  const uint8_t* rimg;
 };
 
 // In-kernel activation quantisation of the streaming kernel: at most
@@ -217,5 +271,20 @@ int tile_gemm_splits(int64_t M, int64_t N, int64_t K);  // K splits the tile ker
 hipError_t launch_tile_gemm(const GemmArgs& a, hipStream_t st);
 // Packed activation codes qa [M][K/2] -> the wide fragment order.
 hipError_t launch_widen_acts(const uint8_t* qa, int64_t M, int64_t K, uint8_t* qaw, hipStream_t st);
+
+// fp6 route: images (layout above) and the tile kernel that reads them.
+// Residual block images: b = 64 or 128, one 1.5 KB piece per 32 rows and
+// 64-code slice of the block, piece (32-row block c, slice u) at
+// (c * (b/64) + u) * 1536, lane l's dwords 0-3 at 16 l and 4-5 at
+// 1024 + 8 l of the piece.
+inline size_t fp6_rows_bytes(int64_t rows, int64_t K) { return (size_t)((rows + 31) / 32) * (size_t)(K / kGroup) * kFp6Frag; }
+inline size_t fp6_residual_bytes(int64_t n_select, int block) { return (size_t)n_select * (size_t)block * block * 3 / 4; }
+hipError_t launch_act_quant_fp6(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* aimg,
+                                float* sa, hipStream_t st);
+hipError_t launch_acts_fp6(const uint8_t* qa, int64_t M, int64_t K, uint8_t* aimg, hipStream_t st);
+hipError_t launch_weights_fp6(const uint8_t* qw, int64_t N, int64_t K, uint8_t* wimg, hipStream_t st);
+hipError_t launch_residual_fp6(const uint8_t* qr, int n_select, int block, uint8_t* rimg, hipStream_t st);
+bool tile6_gemm_fits(const GemmArgs& a);
+hipError_t launch_tile6_gemm(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mq

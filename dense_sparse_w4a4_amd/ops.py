@@ -25,6 +25,8 @@ LIB_PATH = os.path.join(_PKG, "libmosaicq.so")
 
 GROUP = 128
 FLAG_DUMP_ACC = 1
+FLAG_INT8_TILE = 2
+FLAG_FP6_TILE = 4
 
 _c_i64 = ctypes.c_int64
 _c_i32 = ctypes.c_int32
@@ -65,6 +67,13 @@ _SIGS = {
                                               _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "mq_fused_layer_noalloc": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i32,
                                               _c_i32, _vp, _vp, _vp, _vp, _vp, _c_i64, _vp]),
+    "mq_fp6_sizes": (ctypes.c_int, [_c_i64, _c_i64, _c_i64, _c_i32, _c_i32] +
+                     [ctypes.POINTER(ctypes.c_size_t)] * 3),
+    "mq_fp6_prepare_acts": (ctypes.c_int, [_vp, _c_i64, _c_i64, _vp, _vp]),
+    "mq_fp6_prepare_weights": (ctypes.c_int, [_vp, _c_i64, _c_i64, _c_i32, _c_i32, _vp, _vp, _vp]),
+    "mq_fused_gemm_fp6": (ctypes.c_int, [_vp, _vp, _c_i64, _c_i64, _c_i64, _vp, _vp, _c_i32, _c_i32,
+                                         _vp, _vp, _vp, _vp, _c_i64, _vp, ctypes.c_size_t,
+                                         ctypes.c_uint32, _vp, _vp]),
 }
 
 NOALLOC_SCRATCH_BYTES = 128 << 20
@@ -299,11 +308,15 @@ def fused_gemm_workspace(M: int, N: int, K: int) -> int:
 @_on_stream
 def fused_gemm(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer,
                out: Optional[torch.Tensor] = None, dump: bool = False,
-               workspace: Optional[torch.Tensor] = None, stream=None):
+               workspace: Optional[torch.Tensor] = None, stream=None, route: Optional[str] = None):
     """Y fp16 [M, N] = deq(Qa(X) Q(W)^T) + deq(Qa(X) R^T).
 
     With dump=True also returns the exact accumulators
-    (acc_base int32 [M, N, K/128], acc_res int32 [n_select, M, b])."""
+    (acc_base int32 [M, N, K/128], acc_res int32 [n_select, M, b]).
+    route="int8" or "fp6" picks the prefill kernel's route for M > 32
+    (default: fp6 from M = 1024 on, when block is 64 or 128); same y."""
+    if route not in (None, "int8", "fp6"):
+        raise ValueError("route must be None, 'int8' or 'fp6'")
     _dev(qa, torch.uint8, "qa")
     _dev(sa, torch.float32, "sa")
     M = qa.shape[0]
@@ -327,7 +340,8 @@ def fused_gemm(qa: torch.Tensor, sa: torch.Tensor, layer: PackedLayer,
         _ptr(layer.row_ptr) if ns else None, _ptr(layer.col_idx) if ns else None,
         _ptr(layer.qr) if ns else None, _ptr(layer.sr) if ns else None,
         _ptr(out), out.stride(0), _ptr(workspace) if wsb else None, wsb,
-        FLAG_DUMP_ACC if dump else 0, _ptr(acc), _stream(stream)))
+        (FLAG_DUMP_ACC if dump else 0) | {None: 0, "int8": FLAG_INT8_TILE, "fp6": FLAG_FP6_TILE}[route],
+        _ptr(acc), _stream(stream)))
     if dump:
         base = acc[: M * N * G].view(M, N, G)
         res = acc[M * N * G:].view(ns, M, b)
@@ -391,6 +405,79 @@ def fused_layer_noalloc(x: torch.Tensor, layer: PackedLayer, out: torch.Tensor,
         _ptr(layer.row_ptr) if ns else None, _ptr(layer.col_idx) if ns else None,
         _ptr(layer.qr) if ns else None, _ptr(layer.sr) if ns else None,
         _ptr(out), out.stride(0), _stream(stream)))
+    return out
+
+
+def fp6_sizes(M: int, N: int, K: int, block: int, n_select: int):
+    """(activation image, weight image, split-K partials) bytes of the fp6 route."""
+    a, w, p = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    _check("mq_fp6_sizes", lib().mq_fp6_sizes(M, N, K, block, n_select, ctypes.byref(a),
+                                               ctypes.byref(w), ctypes.byref(p)))
+    return int(a.value), int(w.value), int(p.value)
+
+
+@_on_stream
+def fp6_prepare_acts(qa: torch.Tensor, K: int, out: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Packed activation codes [M, K/2] -> the fp6 route's activation image."""
+    _dev(qa, torch.uint8, "qa")
+    M = qa.shape[0]
+    if qa.dim() != 2 or qa.shape[1] * 2 != K or not qa.is_contiguous():
+        raise ValueError("qa must be contiguous [M, K/2]")
+    nbytes = -(-M // 32) * (K // GROUP) * 3072
+    if out is None:
+        out = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=qa.device)
+    _dev(out, torch.uint8, "out")
+    if out.numel() < nbytes:
+        raise ValueError("out is smaller than the activation image")
+    _check("mq_fp6_prepare_acts", lib().mq_fp6_prepare_acts(_ptr(qa), M, K, _ptr(out), _stream(stream)))
+    return out
+
+
+@_on_stream
+def fp6_prepare_weights(layer: PackedLayer, out: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """The packed layer's base and residual codes -> the fp6 weight image."""
+    N, K, b, ns = layer.N, layer.K, layer.block, layer.n_select
+    _, wb, _ = fp6_sizes(0, N, K, b, ns)
+    if out is None:
+        out = torch.empty(wb, dtype=torch.uint8, device=layer.qw.device)
+    _dev(out, torch.uint8, "out")
+    if out.numel() < wb:
+        raise ValueError("out is smaller than the weight image")
+    _check("mq_fp6_prepare_weights", lib().mq_fp6_prepare_weights(
+        _ptr(layer.qw), N, K, b, ns, _ptr(layer.qr) if ns else None, _ptr(out), _stream(stream)))
+    return out
+
+
+@_on_stream
+def fused_gemm_fp6(act_img: torch.Tensor, sa: torch.Tensor, M: int, layer: PackedLayer,
+                   weight_img: torch.Tensor, out: Optional[torch.Tensor] = None, dump: bool = False,
+                   split_ws: Optional[torch.Tensor] = None, stream=None):
+    """fused_gemm on prepared fp6 images (same accumulators, same y bits)."""
+    _dev(act_img, torch.uint8, "act_img")
+    _dev(sa, torch.float32, "sa")
+    _dev(weight_img, torch.uint8, "weight_img")
+    N, K, b, ns = layer.N, layer.K, layer.block, layer.n_select
+    ab, wb, pb = fp6_sizes(M, N, K, b, ns)
+    if act_img.numel() < ab or weight_img.numel() < wb or sa.numel() < M * (K // GROUP):
+        raise ValueError("act_img, weight_img or sa is too small for the shape")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float16, device=sa.device)
+    _dev(out, torch.float16, "out")
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != M or out.shape[1] != N:
+        raise ValueError("out must be [M, N] with unit column stride")
+    if pb and (split_ws is None or split_ws.numel() * split_ws.element_size() < pb):
+        split_ws = torch.empty(pb, dtype=torch.uint8, device=sa.device)
+    G = K // GROUP
+    acc = torch.empty(M * N * G + ns * M * b, dtype=torch.int32, device=sa.device) if dump else None
+    _check("mq_fused_gemm_fp6", lib().mq_fused_gemm_fp6(
+        _ptr(act_img), _ptr(sa), M, N, K, _ptr(weight_img), _ptr(layer.sw), b, ns,
+        _ptr(layer.row_ptr) if ns else None, _ptr(layer.col_idx) if ns else None,
+        _ptr(layer.sr) if ns else None, _ptr(out), out.stride(0), _ptr(split_ws) if pb else None, pb,
+        FLAG_DUMP_ACC if dump else 0, _ptr(acc), _stream(stream)))
+    if dump:
+        return out, acc[: M * N * G].view(M, N, G), acc[M * N * G:].view(ns, M, b)
     return out
 
 
@@ -484,3 +571,7 @@ mq_residual_merge = residual_merge
 mq_smooth_weights = smooth_weights
 mq_smooth_acts = smooth_acts
 mq_measure_mfma = measure_mfma
+mq_fp6_sizes = fp6_sizes
+mq_fp6_prepare_acts = fp6_prepare_acts
+mq_fp6_prepare_weights = fp6_prepare_weights
+mq_fused_gemm_fp6 = fused_gemm_fp6

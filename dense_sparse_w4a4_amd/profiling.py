@@ -31,6 +31,7 @@ COPY_KERNEL = "copyBuffer"
 KERNEL_SOURCES = {
     "gemm_stream_kernel": ["gemm.hip"],
     "gemm_tile_kernel": ["gemm_tile.hip"],
+    "gemm_tile6_kernel": ["gemm_tile6.hip", "fp6.hip"],
 }
 SHARED_SOURCES = ["api.hip", "gemm_common.h", "mq_internal.h"]
 
@@ -105,8 +106,8 @@ def stats(outdir: str, prefix: str, title: str, cmd: str) -> str:
         # benchmark's per-launch average compares with)
         fam = defaultdict(list)
         for (k, _, _), v in per.items():
-            for name in ("gemm_stream_kernel", "gemm_tile_kernel"):
-                if name in k:
+            for name in ("gemm_stream_kernel", "gemm_tile_kernel", "gemm_tile6_kernel"):
+                if name + "<" in k or k.startswith(name):
                     fam[name] += v
         out += ["", "All launches per kernel (every template instance):", "",
                 "| kernel | calls | average (us) | p10 / median / p90 (us) |", "|---|---:|---:|---:|"]

@@ -203,6 +203,12 @@ mq_status mq_select_exact_greedy(const uint16_t* w, const uint16_t* x_calib, int
 
 /* Debug flag for mq_fused_gemm: also store the exact integer accumulators. */
 #define MQ_FLAG_DUMP_ACC 1u
+/* mq_fused_gemm flags choosing the prefill kernel's route (measurement and
+ * cross-checks; both give the same y bits): the int8 route even where the
+ * fp6 route would run, or the fp6 route already from M = 33 (by default
+ * from M = 1024) when the workspace holds its images and block is 64 or 128. */
+#define MQ_FLAG_INT8_TILE 2u
+#define MQ_FLAG_FP6_TILE 4u
 
 /*
  * Bytes of workspace mq_fused_gemm can use for this shape (host output).
@@ -324,6 +330,62 @@ mq_status mq_fused_layer_noalloc(const uint16_t* x, int64_t M, int64_t K, int64_
                                  int32_t n_select, const int32_t* row_ptr, const int32_t* col_idx,
                                  const uint8_t* qr, const uint16_t* sr, uint16_t* y, int64_t ldy,
                                  void* stream);
+
+/*
+ * The prefill kernel's fp6 route with prepared operands.  From M = 1024 on
+ * (block 64 or 128), mq_fused_gemm and mq_fused_layer run the LDS-tiled
+ * kernel on the FP6 matrix core: the 4-bit codes are re-encoded as FP6
+ * E2M3 fields in sign-magnitude, |q| <= 8 in the low five bits, whose value
+ * is exactly q/8, so V_MFMA_F32_32X32X64_F8F6F4 returns the exact integer
+ * dot products / 64 in fp32, at twice the K per cycle of the int8
+ * instruction; y is the int8 route's, bit for bit.  Those calls convert the
+ * weights on every call into their workspace; a caller that can keep the
+ * converted weights (0.75 byte per weight code, 1.5x the packed base, plus
+ * the residual blocks at the same rate) prepares them once here and runs
+ * the kernel alone with mq_fused_gemm_fp6.
+ * [summary-pt Metodologia 3: the dense 4-bit product and the residual run
+ * in one kernel that reuses the staged activation tile.]
+ * Image layout (3 KB per 32 rows and group of 128 codes; rows are tokens or
+ * output channels): for slice u in {0, 1} (codes 64u .. 64u+63 of the
+ * group), lane l = r + 32h (row r, half h) holds codes 64u + 32h + i,
+ * i = 0..31, as six-bit fields at bit 6i of six dwords: dwords 0-3 at byte
+ * u*1024 + 16l, dwords 4-5 at 2048 + u*512 + 8l.  The weight image is the
+ * base, [N/32][K/128][3 KB], then from byte round_up(N*K*3/4, 256) the
+ * residual blocks in CSR order, b*b*3/4 bytes each: per 32 rows c and
+ * slice u of the block a 1536-byte piece at (c*(b/64) + u)*1536, lane l's
+ * dwords 0-3 at 16l, 4-5 at 1024 + 8l.
+ */
+
+/* Sizes of the fp6 route's buffers (host outputs): the activation image of
+ * M tokens ([ceil(M/32)][K/128][3 KB]), the weight image (base + residual)
+ * and mq_fused_gemm_fp6's split-K partials (0 when no split applies).
+ * block must be 64 or 128 (MQ_ERR_BLOCK); M*K and N*K below 2^32. */
+mq_status mq_fp6_sizes(int64_t M, int64_t N, int64_t K, int32_t block, int32_t n_select,
+                       size_t* act_bytes, size_t* weight_bytes, size_t* split_bytes);
+
+/* Packed activation codes qa [M][K/2] (as from mq_quantize_act) -> the
+ * activation image act_img (mq_fp6_sizes' act_bytes, 16-byte aligned; rows
+ * past M up to a multiple of 32 are written as zeros). */
+mq_status mq_fp6_prepare_acts(const uint8_t* qa, int64_t M, int64_t K, uint8_t* act_img,
+                              void* stream);
+
+/* Packed base qw (slab layout) and residual qr (as from mq_pack_weights)
+ * -> weight_img (mq_fp6_sizes' weight_bytes, 16-byte aligned).  qr may be
+ * NULL when n_select == 0. */
+mq_status mq_fp6_prepare_weights(const uint8_t* qw, int64_t N, int64_t K, int32_t block,
+                                 int32_t n_select, const uint8_t* qr, uint8_t* weight_img,
+                                 void* stream);
+
+/* mq_fused_gemm on prepared images: the same accumulators and the same y
+ * bits.  M == 0 or M > 32 (the tile kernel's range); block 64 or 128;
+ * split_ws holds mq_fp6_sizes' split_bytes (may be NULL when that is 0);
+ * flags 0 or MQ_FLAG_DUMP_ACC (acc_dump as for mq_fused_gemm).  A K whose
+ * residual table does not fit the kernel's LDS gives MQ_ERR_SHAPE. */
+mq_status mq_fused_gemm_fp6(const uint8_t* act_img, const float* sa, int64_t M, int64_t N, int64_t K,
+                            const uint8_t* weight_img, const uint16_t* sw, int32_t block,
+                            int32_t n_select, const int32_t* row_ptr, const int32_t* col_idx,
+                            const uint16_t* sr, uint16_t* y, int64_t ldy, void* split_ws,
+                            size_t split_bytes, uint32_t flags, int32_t* acc_dump, void* stream);
 
 /*
  * Unfused ablation (measurement only; the layer's path never needs it): the

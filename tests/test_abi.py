@@ -99,7 +99,8 @@ def _gemm(L, **kw):
 
 
 def test_fused_gemm_validation(L):
-    assert _gemm(L, flags=4) == ARG
+    assert _gemm(L, flags=8) == ARG
+    assert _gemm(L, flags=2 | 4) == ARG  # the int8 and fp6 routes exclude each other
     assert _gemm(L, b=100) == BLOCK
     assert _gemm(L, M=-3) == SHAPE
     assert _gemm(L, N=100) == SHAPE
@@ -268,3 +269,36 @@ def test_exact_selection_validation(L):
     assert dcall(dist=None) == NULLP
     assert dcall(x=PMIS) == ALIGN
     assert dcall(wsb=4096) == WS
+
+
+def test_fp6_route_validation(L):
+    a, w, p = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
+    sz = lambda *args: L.mq_fp6_sizes(*args, ctypes.byref(a), ctypes.byref(w), ctypes.byref(p))  # noqa: E731
+    assert sz(4096, 5120, 25600, 64, 3200) == OK
+    assert a.value == 4096 // 32 * 200 * 3072
+    assert w.value == 5120 * 25600 * 3 // 4 + 3200 * 64 * 64 * 3 // 4  # (base a multiple of 256)
+    assert p.value == 0
+    assert sz(300, 256, 2048, 64, 10) == OK and p.value == 300 * 256 * 4 * 2  # two K splits
+    assert sz(4096, 5120, 25600, 32, 0) == BLOCK
+    assert sz(4096, 5120, 25600, 64, 10 ** 6) == BUDGET
+    assert sz(4096, 5000, 25600, 64, 0) == SHAPE
+    assert L.mq_fp6_sizes(64, 64, 128, 64, 0, None, None, None) == NULLP
+    prep = L.mq_fp6_prepare_weights
+    assert prep(P, 64, 128, 32, 0, None, P, None) == BLOCK
+    assert prep(None, 64, 128, 64, 0, None, P, None) == NULLP
+    assert prep(P, 64, 128, 64, 1, None, P, None) == NULLP
+    assert prep(PMIS, 64, 128, 64, 0, None, P, None) == ALIGN
+    assert L.mq_fp6_prepare_acts(P, 64, 100, P, None) == SHAPE
+    assert L.mq_fp6_prepare_acts(None, 64, 128, P, None) == NULLP
+    g = lambda **kw: L.mq_fused_gemm_fp6(  # noqa: E731
+        kw.get("ai", P), P, kw.get("M", 64), kw.get("N", 128), kw.get("K", 256), P, P, kw.get("b", 64), 0,
+        None, None, None, P, kw.get("ldy", 128), kw.get("ws", None), kw.get("wsb", 0),
+        kw.get("flags", 0), None, None)
+    assert g(M=16) == SHAPE
+    assert g(b=32) == BLOCK
+    assert g(flags=2) == ARG
+    assert g(flags=1) == NULLP  # dump without acc_dump
+    assert g(ai=None) == NULLP
+    assert g(ldy=100) == SHAPE
+    assert g(M=300, N=256, K=2048, ldy=256) == WS  # split-K partials needed, none given
+    assert g(M=0) == OK

@@ -77,6 +77,38 @@ def test_fused_layer_matches_two_kernels_and_oracle(M, N, K, b, rho, one_kernel)
     assert_y_close(y, ref["y"])
 
 
+FP6_CASES = [
+    # M, N, K, b, rho: the prefill kernel (the layer takes the fp6 route from
+    # M = 1024 when b is 64 or 128): ragged token and channel tiles, split-K,
+    # a second token band
+    (300, 256, 2048, 64, 0.10),
+    (1100, 640, 768, 64, 0.15),
+    (1024, 128, 4096, 128, 0.20),
+    (1300, 256, 1536, 64, 0.10),
+]
+
+
+@pytest.mark.parametrize("M,N,K,b,rho", FP6_CASES)
+def test_fused_layer_fp6_route_matches_int8_route_and_oracle(M, N, K, b, rho):
+    # The fp6 route (act-quant into FP6 images, weight and residual
+    # conversion, fp6 tile kernel) gives the int8 route's y bit for bit: the
+    # two form the same products sa*sw*dot, scaled by powers of two.
+    print(f"case M={M} N={N} K={K} b={b} rho={rho}", flush=True)
+    spec = syn.LayerSpec("f6", K=K, N=N, w_outlier_frac=0.01, x_outlier_count=3, T=32, block=b, rho=rho)
+    w, xc, layer = _gpu_layer(spec, seed=M + N)
+    x = syn.make_acts(spec, M, seed=K)
+    xt = dev(x)
+    y = ops.fused_layer(xt, layer)
+    qa, sa = ops.quantize_act(xt)
+    y6 = ops.fused_gemm(qa, sa, layer, route="fp6")
+    y8 = ops.fused_gemm(qa, sa, layer, route="int8")
+    torch.cuda.synchronize()
+    assert np.array_equal(_bits(y), _bits(y8))
+    assert np.array_equal(_bits(y6), _bits(y8))
+    ref = oracle.layer_reference(x, w, xc, b, spec.n_select)
+    assert_y_close(y, ref["y"])
+
+
 def test_fused_layer_special_values_and_padded_rows():
     # all-zero groups, an infinite value (its group's codes are 0 and y is NaN
     # on that row on both routes), subnormals, fp16 extremes, exact .5 ties

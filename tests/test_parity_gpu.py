@@ -189,6 +189,35 @@ def test_fused_gemm_accumulators_exact_and_y(M, N, K, b, rho):
     assert np.array_equal(host(y2).view(np.uint16), host(y).view(np.uint16))
 
 
+@pytest.mark.parametrize("M,N,K,b,rho", [(257, 192, 256, 64, 0.15), (300, 256, 2048, 64, 0.10),
+                                         (64, 128, 1024, 128, 0.25), (40, 128, 3200, 64, 0.10),
+                                         (513, 640, 1536, 64, 0.20), (1000, 384, 640, 128, 0.10),
+                                         (1030, 256, 1024, 64, 0.10)])
+def test_fp6_route_matches_int8_route(M, N, K, b, rho):
+    # the prefill kernel's two routes on the same codes: identical exact
+    # accumulators and identical y bits, with and without the dump
+    print(f"fp6 vs int8 M={M} N={N} K={K} b={b} rho={rho}", flush=True)
+    spec = syn.LayerSpec("r", K=K, N=N, w_outlier_frac=0.01, x_outlier_count=3,
+                         T=32, block=b, rho=rho)
+    w, xc = _layer(spec, seed=M + 7)
+    x = syn.make_acts(spec, M, seed=N)
+    rsel, _, _ = oracle.select_blocks(w, xc, b, spec.n_select)
+    ref = oracle.pack_weights(w, b, rsel)
+    rqa, rsa = oracle.quantize_act(x)
+    layer = ops.PackedLayer(N, K, b, dev(ref["qw"]), dev(ref["sw"]), dev(ref["row_ptr"]),
+                            dev(ref["col_idx"]), dev(ref["qr"]), dev(ref["sr"]))
+    qa, sa = dev(oracle.pack_nibbles(rqa)), dev(rsa)
+    y6, a6, r6 = ops.fused_gemm(qa, sa, layer, dump=True, route="fp6")
+    y8, a8, r8 = ops.fused_gemm(qa, sa, layer, dump=True, route="int8")
+    z6 = ops.fused_gemm(qa, sa, layer, route="fp6")
+    z8 = ops.fused_gemm(qa, sa, layer, route="int8")
+    torch.cuda.synchronize()
+    assert torch.equal(a6, a8) and torch.equal(r6, r8)
+    assert np.array_equal(host(y6).view(np.uint16), host(y8).view(np.uint16))
+    assert np.array_equal(host(z6).view(np.uint16), host(z8).view(np.uint16))
+    assert np.array_equal(host(z6).view(np.uint16), host(y6).view(np.uint16))
+
+
 def test_end_to_end_tiny_and_determinism():
     spec = syn.TINY
     x = syn.make_acts(spec, syn.TINY_M)
@@ -363,6 +392,13 @@ def test_full_nibble_range(M, b):
     assert torch.equal(torch.cat([base.reshape(-1), res.reshape(-1)]), acc1)
     assert_y_close(y, y_ref)
     assert_y_close(y1, y_ref)
+    if M > 32 and b != 32:
+        # the fp6 route: -8 is the one code whose field leaves the subnormal
+        # range (|q| = 8, exponent field 1)
+        y6, base6, res6 = ops.fused_gemm(qa, sa, layer, dump=True, route="fp6")
+        torch.cuda.synchronize()
+        assert torch.equal(base6, base) and torch.equal(res6, res)
+        assert np.array_equal(host(y6).view(np.uint16), host(y).view(np.uint16))
 
 
 @pytest.mark.parametrize("M,b", [(16, 64), (300, 32), (70, 128)])
