@@ -260,6 +260,13 @@ static size_t wide_workspace(int64_t M, int64_t K) {
   return round256((size_t)wide_rows(M) * (size_t)K);
 }
 
+// Split-K partials of the fp6 route (its own split rule).
+static size_t split6_workspace(int64_t M, int64_t N, int64_t K) {
+  if (M <= 32 || N <= 0 || K < kGroup) return 0;
+  const int ks = tile6_gemm_splits(M, N, K);
+  return ks > 1 ? (size_t)ks * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
 // mq_fused_gemm's workspace on the int8 route: the wide activation codes,
 // then the split-K partials.
 static size_t gemm_workspace_i8(int64_t M, int64_t N, int64_t K) {
@@ -281,7 +288,7 @@ static size_t fp6_images_bound(int64_t M, int64_t N, int64_t K) {
 }
 static size_t gemm_workspace(int64_t M, int64_t N, int64_t K) {
   const size_t i8 = gemm_workspace_i8(M, N, K);
-  const size_t f6 = M >= kFp6MinM ? fp6_images_bound(M, N, K) + split_workspace(M, N, K) : 0;
+  const size_t f6 = M >= kFp6MinM ? fp6_images_bound(M, N, K) + split6_workspace(M, N, K) : 0;
   return i8 > f6 ? i8 : f6;
 }
 
@@ -369,7 +376,8 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
   // to LDS without widening, and the split-K schedule is used where it
   // applies.  Otherwise one pass over K from the packed codes.
   const size_t split = split_workspace(M, N, K);
-  const size_t need6 = M > 32 ? fp6_images_bytes(M, N, K, block, n_select) + split : 0;
+  const size_t split6 = split6_workspace(M, N, K);
+  const size_t need6 = M > 32 ? fp6_images_bytes(M, N, K, block, n_select) + split6 : 0;
   const size_t need = gemm_workspace_i8(M, N, K);
   const int64_t min_m6 = (flags & MQ_FLAG_FP6_TILE) ? 33 : kFp6MinM;
   const bool fp6 = !(flags & MQ_FLAG_INT8_TILE) && M >= min_m6 && workspace && workspace_bytes >= need6 &&
@@ -382,8 +390,8 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
     st = hip_status(launch_acts_fp6(qa, M, K, const_cast<uint8_t*>(a.aimg), (hipStream_t)stream),
                     "mq_fused_gemm fp6 conversion launch");
     if (st != MQ_OK) return st;
-    a.part = split > 0 ? reinterpret_cast<float*>(ws + need6 - split) : nullptr;
-    a.ksplit = split > 0 ? tile_gemm_splits(M, N, K) : 1;
+    a.part = split6 > 0 ? reinterpret_cast<float*>(ws + need6 - split6) : nullptr;
+    a.ksplit = split6 > 0 ? tile6_gemm_splits(M, N, K) : 1;
   } else if (wide) {
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     const mq_status st = hip_status(launch_widen_acts(qa, M, K, ws, (hipStream_t)stream),
@@ -413,12 +421,12 @@ static size_t layer_workspace_i8(int64_t M, int64_t N, int64_t K) {
 // The fp6 route: the activation scales, the fp6 images, the split-K partials.
 static size_t layer_scales_bytes(int64_t M, int64_t K) { return round256((size_t)M * (size_t)(K / kGroup) * 4); }
 static size_t layer_workspace_fp6(int64_t M, int64_t N, int64_t K, int block, int64_t n_select) {
-  return layer_scales_bytes(M, K) + fp6_images_bytes(M, N, K, block, n_select) + split_workspace(M, N, K);
+  return layer_scales_bytes(M, K) + fp6_images_bytes(M, N, K, block, n_select) + split6_workspace(M, N, K);
 }
 static size_t layer_workspace(int64_t M, int64_t N, int64_t K) {
   const size_t i8 = layer_workspace_i8(M, N, K);
   if (M < kFp6MinM || N <= 0 || K < kGroup) return i8;
-  const size_t f6 = layer_scales_bytes(M, K) + fp6_images_bound(M, N, K) + split_workspace(M, N, K);
+  const size_t f6 = layer_scales_bytes(M, K) + fp6_images_bound(M, N, K) + split6_workspace(M, N, K);
   return i8 > f6 ? i8 : f6;
 }
 
@@ -510,6 +518,7 @@ static mq_status layer_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
     return hip_status(launch_fused_gemm(a, st), "mq_fused_layer launch");
   }
   const size_t split = split_workspace(M, N, K);
+  const size_t split6 = split6_workspace(M, N, K);
   if (M >= kFp6MinM && tile6_gemm_fits(a) && ws_bytes >= layer_workspace_fp6(M, N, K, block, n_select)) {
     // fp6 tile kernel: scales, then the images
     float* sa6 = reinterpret_cast<float*>(ws);
@@ -520,9 +529,9 @@ static mq_status layer_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
     s = hip_status(launch_act_quant_fp6(x, M, K, ldx, const_cast<uint8_t*>(a.aimg), sa6, st),
                    "mq_fused_layer act-quant launch");
     if (s != MQ_OK) return s;
-    if (split > 0) {
-      a.part = reinterpret_cast<float*>(ws + layer_workspace_fp6(M, N, K, block, n_select) - split);
-      a.ksplit = tile_gemm_splits(M, N, K);
+    if (split6 > 0) {
+      a.part = reinterpret_cast<float*>(ws + layer_workspace_fp6(M, N, K, block, n_select) - split6);
+      a.ksplit = tile6_gemm_splits(M, N, K);
     }
     return hip_status(launch_fused_gemm(a, st), "mq_fused_layer launch");
   }
@@ -777,7 +786,7 @@ mq_status mq_fp6_sizes(int64_t M, int64_t N, int64_t K, int32_t block, int32_t n
   if (s != MQ_OK) return s;
   *act_bytes = fp6_rows_bytes(M, K);
   *weight_bytes = round256(fp6_rows_bytes(N, K)) + fp6_residual_bytes(n_select, block);
-  *split_bytes = split_workspace(M, N, K);
+  *split_bytes = split6_workspace(M, N, K);
   return MQ_OK;
 }
 
@@ -829,7 +838,7 @@ mq_status mq_fused_gemm_fp6(const uint8_t* act_img, const float* sa, int64_t M, 
                  aligned16(row_ptr) && aligned16(col_idx) && aligned16(sr) && aligned16(split_ws) &&
                  aligned16(acc_dump),
              MQ_ERR_ALIGN, "device pointers must be 16-byte aligned");
-  const size_t split = split_workspace(M, N, K);
+  const size_t split = split6_workspace(M, N, K);
   MQ_REQUIRE(split == 0 || (split_ws && split_bytes >= split), MQ_ERR_WORKSPACE,
              "split-K workspace of %zu bytes given, %zu needed", split_bytes, split);
   GemmArgs a = {};
@@ -853,7 +862,7 @@ mq_status mq_fused_gemm_fp6(const uint8_t* act_img, const float* sa, int64_t M, 
   MQ_REQUIRE(tile6_gemm_fits(a), MQ_ERR_SHAPE, "K = %lld too long for the fp6 kernel's residual table",
              (long long)K);
   a.part = split > 0 ? static_cast<float*>(split_ws) : nullptr;
-  a.ksplit = split > 0 ? tile_gemm_splits(M, N, K) : 1;
+  a.ksplit = split > 0 ? tile6_gemm_splits(M, N, K) : 1;
   return hip_status(launch_tile6_gemm(a, (hipStream_t)stream), "mq_fused_gemm_fp6 launch");
 }
 

@@ -38,7 +38,7 @@ __global__ __launch_bounds__(256) void act_quant_fp6_kernel(const uint16_t* __re
   amax = row16_max(amax);
   const float s = amax / 7.0f;
   const float r = s == 0.0f ? 0.0f : 1.0f / s;
-  const uint64_t own = fp6_fields8(quant4_word(f, s, r));
+  const uint64_t own = quant4_fields8(f, s, r);
   const uint32_t plo = (uint32_t)__shfl_xor((int)(uint32_t)own, 1, 16);
   const uint32_t phi = (uint32_t)__shfl_xor((int)(uint32_t)(own >> 32), 1, 16);
   if ((t & 1) == 0) {

@@ -485,6 +485,31 @@ hipError_t launch_tile6_cfg(const GemmArgs& a, hipStream_t st) {
 
 }  // namespace
 
+// K splits of the fp6 route: the fewest splits within 3% of the best
+// estimate of whole rounds of one 512-thread workgroup per CU times groups
+// per workgroup (about 1.4 us per group) plus the fp32 partials' round trip
+// through HBM (written once, read once, at about 5 TB/s).  Unlike the int8
+// route's rule it also splits when the tiles leave a partial last round
+// (Qwen3-32B 25600 x 5120 at M = 4096: 640 tiles, 2.5 rounds -> 2 splits,
+// 5 rounds of half the groups), at least 8 groups per split.
+int tile6_gemm_splits(int64_t M, int64_t N, int64_t K) {
+  constexpr double kCUs = 256.0, kGroupSec = 1.4e-6, kHbm = 5.0e12;
+  const int64_t tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
+  const int64_t G = K / kGroup;
+  double best = 0.0;
+  int bk = 1;
+  for (int ks = 1; ks <= 8 && (ks == 1 || G / ks >= 8); ++ks) {
+    const double rounds = (double)((tiles * ks + (int64_t)kCUs - 1) / (int64_t)kCUs);
+    const double t = rounds * (double)((G + ks - 1) / ks) * kGroupSec +
+                     (ks > 1 ? (double)(ks + 1) * (double)M * (double)N * 4.0 / kHbm : 0.0);
+    if (ks == 1 || t < best * 0.97) {
+      best = t;
+      bk = ks;
+    }
+  }
+  return bk;
+}
+
 // The fp6 route covers blocks of 64 and 128 (a block of 32 is half a 64-code
 // slice, whose other half would belong to another block) and K whose
 // residual table fits in LDS.

@@ -128,6 +128,30 @@ __device__ __forceinline__ uint64_t fp6_fields8(uint32_t w) {
   return r;
 }
 
+// quant4_word's eight codes written directly as FP6 fields (field i at bits
+// 6i of the result): the same reciprocal quotient, rint and clamp, then
+// |q| | (q < 0) << 5 (a code of -0.0 counts as 0); every field 0 for an
+// infinite scale.
+__device__ __forceinline__ uint64_t quant4_fields8(const float f[8], float s, float r) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const float q0 = f[i] * r;
+    const float e = fmaf(-q0, s, f[i]);
+    const float q = fminf(fmaxf(rintf(fmaf(e, r, q0)), -7.0f), 7.0f);
+    const uint32_t fld = (uint32_t)fabsf(q) | (q < 0.0f ? 32u : 0u);
+    if (6 * i + 6 <= 32) {
+      lo |= fld << (6 * i);
+    } else if (6 * i >= 32) {
+      hi |= fld << (6 * i - 32);
+    } else {
+      lo |= fld << (6 * i);
+      hi |= fld >> (32 - 6 * i);
+    }
+  }
+  return s < __builtin_inff() ? ((uint64_t)hi << 32) | lo : 0u;
+}
+
 // 32 codes (four words, code i in nibble i % 8 of word i / 8) -> the six
 // operand dwords of one lane.
 __device__ __forceinline__ void fp6_fields32(const uint32_t w[4], uint32_t d[6]) {
@@ -285,6 +309,7 @@ hipError_t launch_acts_fp6(const uint8_t* qa, int64_t M, int64_t K, uint8_t* aim
 hipError_t launch_weights_fp6(const uint8_t* qw, int64_t N, int64_t K, uint8_t* wimg, hipStream_t st);
 hipError_t launch_residual_fp6(const uint8_t* qr, int n_select, int block, uint8_t* rimg, hipStream_t st);
 bool tile6_gemm_fits(const GemmArgs& a);
+int tile6_gemm_splits(int64_t M, int64_t N, int64_t K);  // K splits of the fp6 route
 hipError_t launch_tile6_gemm(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mq

@@ -274,10 +274,12 @@ def test_exact_selection_validation(L):
 def test_fp6_route_validation(L):
     a, w, p = ctypes.c_size_t(0), ctypes.c_size_t(0), ctypes.c_size_t(0)
     sz = lambda *args: L.mq_fp6_sizes(*args, ctypes.byref(a), ctypes.byref(w), ctypes.byref(p))  # noqa: E731
-    assert sz(4096, 5120, 25600, 64, 3200) == OK
-    assert a.value == 4096 // 32 * 200 * 3072
+    assert sz(4096, 25600, 5120, 64, 3200) == OK
+    assert a.value == 4096 // 32 * 40 * 3072
     assert w.value == 5120 * 25600 * 3 // 4 + 3200 * 64 * 64 * 3 // 4  # (base a multiple of 256)
-    assert p.value == 0
+    assert p.value == 0  # 3200 tiles: 12.5 rounds, no split
+    assert sz(4096, 5120, 25600, 64, 3200) == OK
+    assert p.value == 2 * 4096 * 5120 * 4  # 640 tiles, 2.5 rounds: two splits, 5 rounds
     assert sz(300, 256, 2048, 64, 10) == OK and p.value == 300 * 256 * 4 * 2  # two K splits
     assert sz(4096, 5120, 25600, 32, 0) == BLOCK
     assert sz(4096, 5120, 25600, 64, 10 ** 6) == BUDGET

@@ -140,8 +140,8 @@ def test_gemm_on_prepared_images(M, N, K, b, frac):
 
 def test_full_size_qwen3_32b_prefill_prepared():
     # the configured Qwen3-32B MLP shapes at M = 4096 (the kernel the default
-    # benchmark times): prepared route against the int8 route, bit for bit,
-    # and sampled block rows against the oracle's accumulators
+    # benchmark times): prepared route against the one-call layer and the
+    # int8 route
     for K, N in syn.QWEN3_32B_SHAPES:
         M = 4096
         print(f"fp6 full size K={K} N={N} M={M}", flush=True)
@@ -158,7 +158,18 @@ def test_full_size_qwen3_32b_prefill_prepared():
         y8 = ops.fused_gemm(qa, sa, layer, route="int8")
         yl = ops.fused_layer(x, layer)
         torch.cuda.synchronize()
-        assert np.array_equal(host(y6).view(np.uint16), host(y8).view(np.uint16))
-        assert np.array_equal(host(yl).view(np.uint16), host(y8).view(np.uint16))
+        # the layer and the prepared GEMM: the same route and K split
+        assert np.array_equal(host(yl).view(np.uint16), host(y6).view(np.uint16))
+        # the int8 route: bit for bit where both run one K split; 25600 x 5120
+        # is split in two on the fp6 route only (a partial last round
+        # otherwise), which changes the fp32 summation order, so y may move
+        # by one fp16 rounding there (plus the fp32 order's own rounding,
+        # ~1e-6 of the output's rms, where y nearly cancels)
+        a6, a8 = host(y6).astype(np.float64), host(y8).astype(np.float64)
+        if K == 25600:
+            assert_y_close(y6, a8, tol=2.0 ** -10)
+            assert np.mean(a6 == a8) > 0.9
+        else:
+            assert np.array_equal(host(y6).view(np.uint16), host(y8).view(np.uint16))
         del wimg, aimg, y6, y8, yl, layer
         torch.cuda.empty_cache()
