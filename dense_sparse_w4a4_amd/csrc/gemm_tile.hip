@@ -474,7 +474,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
   // register loads: weights, scale, residual codes, residual scale) has
   // completed
   auto dma_wait = [&]() {
-    if constexpr (AW) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    if constexpr (AW) {
+      // the builtin rather than inline asm, so that the compiler's own wait
+      // analysis knows every older load is done
+      __builtin_amdgcn_s_waitcnt(kWaitVm4);
+      asm volatile("" ::: "memory");
+    }
   };
 
   // Two LDS stages: group j is computed from stage j%2 while the waves
@@ -494,19 +499,25 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
   dma_wait();
   lds_barrier();
   // one exit only, so the accumulators need no copies on the back edge
+  // Each step first stores the next group's register-staged operands (their
+  // loads were issued two steps earlier and no DMA is in flight), then
+  // issues the next group's activation DMA, then computes: a store after the
+  // DMA would make the compiler wait for every outstanding load (vmcnt(0))
+  // before its LDS writes, the DMA included, exposing its latency in every
+  // step.
   int j = jb;
   for (; j + 1 < je; j += 2) {
-    dma(st1, j + 1);
-    compute(st0, j);
 #pragma unroll
     for (int part = 0; part < 4; ++part) store_part(st1, R1, min(j + 1, je - 1), part);  // group j+1
+    dma(st1, j + 1);
+    compute(st0, j);
     load(R1, j + 3);
     dma_wait();
     lds_barrier();
-    dma(st0, j + 2);
-    compute(st1, j + 1);
 #pragma unroll
     for (int part = 0; part < 4; ++part) store_part(st0, R0, min(j + 2, je - 1), part);  // group j+2
+    dma(st0, j + 2);
+    compute(st1, j + 1);
     load(R0, j + 4);
     dma_wait();
     lds_barrier();

@@ -222,8 +222,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
     if (wave < 4) __builtin_amdgcn_global_load_lds(srcB1 + jo, (lds_ptr)(uintptr_t)(st + dstB1), 16, 0, 0);
   };
   // after a step's loads: the step's DMA (issued before the step's four
-  // register loads: scale, residual pieces, residual scale) has completed
-  auto dma_wait = [&]() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
+  // register loads: scale, residual pieces, residual scale) has completed.
+  // The builtin (vmcnt 4; expcnt, lgkmcnt unconstrained) rather than inline
+  // asm, so that the compiler's own wait analysis knows every older load is
+  // done and adds no vmcnt(0) before the next step's stores.
+  auto dma_wait = [&]() {
+    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    asm volatile("" ::: "memory");
+  };
 
   // ---- register staging: scales, residual pieces ----
   // Residual: wave w stages column block cbw = w / 2, slice uw = w % 2 of
@@ -419,17 +425,22 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
   load(R0, jb + 2);
   dma_wait();
   lds_barrier();
+  // Each step first stores the next group's register-staged pieces (their
+  // loads were issued two steps earlier and no DMA is in flight), then
+  // issues the next group's DMA, then computes: a store after the DMA would
+  // make the compiler wait for every outstanding load (vmcnt(0)) before its
+  // LDS writes, the DMA included, exposing its whole latency in every step.
   int j = jb;
   for (; j + 1 < je; j += 2) {
+    store(st1, R1, min(j + 1, je - 1));
     dma(st1, j + 1);
     compute(st0, j);
-    store(st1, R1, min(j + 1, je - 1));
     load(R1, j + 3);
     dma_wait();
     lds_barrier();
+    store(st0, R0, min(j + 2, je - 1));
     dma(st0, j + 2);
     compute(st1, j + 1);
-    store(st0, R0, min(j + 2, je - 1));
     load(R0, j + 4);
     dma_wait();
     lds_barrier();
@@ -455,15 +466,25 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
     }
 }
 
-// Split-K reduce: y = fp16(sum of the splits' fp32 partials, in split order).
+// Split-K reduce: y = fp16(sum of the splits' fp32 partials, in split order),
+// four consecutive outputs per thread (N is a multiple of 32): 16-byte
+// partial loads, one 8-byte store.
 __global__ __launch_bounds__(256) void split_reduce6_kernel(const float* __restrict__ part, int ksplit, int64_t M,
                                                             int64_t N, uint16_t* y, int64_t ldy) {
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (idx >= M * N) return;
   const int64_t m = idx / N, n = idx - m * N;
-  float s = 0.f;
-  for (int k = 0; k < ksplit; ++k) s += part[((int64_t)k * M + m) * N + n];
-  y[m * ldy + n] = f2h_bits(s);
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int k = 0; k < ksplit; ++k) {
+    const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)k * M + m) * N + n);
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  const uint32_t lo = (uint32_t)f2h_bits(s.x) | ((uint32_t)f2h_bits(s.y) << 16);
+  const uint32_t hi = (uint32_t)f2h_bits(s.z) | ((uint32_t)f2h_bits(s.w) << 16);
+  *reinterpret_cast<uint2*>(y + m * ldy + n) = make_uint2(lo, hi);
 }
 
 template <int BLK, bool DUMP>
@@ -478,7 +499,7 @@ hipError_t launch_tile6_cfg(const GemmArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * a.ksplit)), dim3(NTHR), lds, st, a);
   e = hipGetLastError();
   if (e != hipSuccess || a.ksplit == 1) return e;
-  hipLaunchKernelGGL(split_reduce6_kernel, dim3((unsigned)((a.M * a.N + 255) / 256)), dim3(256), 0, st, a.part,
+  hipLaunchKernelGGL(split_reduce6_kernel, dim3((unsigned)((a.M * a.N / 4 + 255) / 256)), dim3(256), 0, st, a.part,
                      a.ksplit, a.M, a.N, a.y, a.ldy);
   return hipGetLastError();
 }
