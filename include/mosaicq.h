@@ -217,7 +217,11 @@ mq_status mq_select_exact_greedy(const uint16_t* w, const uint16_t* x_calib, int
  * 256), then, when the 256 x 128 output tiles alone would leave compute
  * units idle, fp32 partial outputs [splits][M][N] of the K groups split
  * over several workgroups, summed by a second kernel in split order (so y
- * stays deterministic).  Sizes the GEMM does not accept (each below 2^31,
+ * stays deterministic).  From M = 1024 it is the larger room of the fp6
+ * route (see mq_fp6_sizes): the FP6 images of the activation codes, the
+ * base and the residual (bounded by every block selected, 0.75*N*K bytes,
+ * since block and n_select are not arguments here) and that route's
+ * split-K partials.  Sizes the GEMM does not accept (each below 2^31,
  * packed weights and activations each below 4 GiB) give MQ_ERR_SHAPE.
  */
 mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes);
@@ -246,15 +250,18 @@ mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes
  *              unspecified but finite y.  Check a CSR with mq_validate_csr.
  *   y        : fp16 [M][ldy], ldy >= N, ldy % 8 == 0 (output)
  *   workspace: device buffer of workspace_bytes (16-byte aligned) or NULL.
- *              With at least mq_fused_gemm_workspace's bytes (M > 32) the
- *              codes are first widened into it for the prefill kernel and
- *              the split-K schedule is used where it applies; with less, or
- *              NULL, the kernel reads the packed codes in one pass over K
- *              (same accumulators, y the same up to fp32 summation order,
- *              slower).
+ *              With enough for the fp6 route (M >= 1024, block 64 or 128)
+ *              the codes, base and residual are re-encoded into it and the
+ *              fp6 kernel runs; otherwise, with at least the int8 route's
+ *              bytes (M > 32) the codes are widened into it for the int8
+ *              kernel; the split-K schedule is used where it applies; with
+ *              less, or NULL, the kernel reads the packed codes in one pass
+ *              over K (same accumulators, y the same up to fp32 summation
+ *              order, slower).
  *              The call owns it until the stream has drained.
  *   Also:      N*K/2 and M*K/2 must each be below 2^32 (MQ_ERR_SHAPE).
- *   flags    : 0 or MQ_FLAG_DUMP_ACC
+ *   flags    : 0 or MQ_FLAG_DUMP_ACC, with at most one of
+ *              MQ_FLAG_INT8_TILE / MQ_FLAG_FP6_TILE
  *   acc_dump : with MQ_FLAG_DUMP_ACC, int32 [M*N*(K/128) + n_select*M*block]:
  *              acc_base as [M][N][K/128] followed by acc_res as
  *              [n_select][M][block]; otherwise ignored (may be NULL)
@@ -275,7 +282,10 @@ mq_status mq_fused_gemm(const uint8_t* qa, const float* sa, int64_t M, int64_t N
  * activation codes (in the layout the GEMM kernel reads best: 16-token tiles
  * for the decode kernel above 8 tokens, room for M padded to a multiple of
  * 16 up to M = 32; the wide fragment order for the prefill kernel), their
- * scales and the split-K partials.
+ * scales and the split-K partials; from M = 1024 the larger room of the fp6
+ * route (scales, FP6 images of the activations, base and residual, the
+ * residual bounded by 0.75*N*K bytes, and its split-K partials), which
+ * mq_fused_layer then uses when block is 64 or 128.
  */
 mq_status mq_fused_layer_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes);
 
