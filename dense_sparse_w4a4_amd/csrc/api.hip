@@ -520,15 +520,20 @@ static mq_status layer_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
   const size_t split = split_workspace(M, N, K);
   const size_t split6 = split6_workspace(M, N, K);
   if (M >= kFp6MinM && tile6_gemm_fits(a) && ws_bytes >= layer_workspace_fp6(M, N, K, block, n_select)) {
-    // fp6 tile kernel: scales, then the images
+    // fp6 tile kernel: scales, then the images (act-quant into the
+    // activation image and the base and residual conversions in one launch)
     float* sa6 = reinterpret_cast<float*>(ws);
     a.sa = sa6;
-    mq_status s = hip_status(fp6_prepare(a, ws + layer_scales_bytes(M, K), st),
-                             "mq_fused_layer fp6 conversion launch");
+    uint8_t* aimg = ws + layer_scales_bytes(M, K);
+    uint8_t* wimg = aimg + round256(fp6_rows_bytes(M, K));
+    uint8_t* rimg = wimg + round256(fp6_rows_bytes(N, K));
+    const mq_status s = hip_status(launch_fp6_layer_prep(x, M, K, ldx, aimg, sa6, qw, N, wimg, a.qr, n_select,
+                                                         block, rimg, st),
+                                   "mq_fused_layer fp6 preparation launch");
     if (s != MQ_OK) return s;
-    s = hip_status(launch_act_quant_fp6(x, M, K, ldx, const_cast<uint8_t*>(a.aimg), sa6, st),
-                   "mq_fused_layer act-quant launch");
-    if (s != MQ_OK) return s;
+    a.aimg = aimg;
+    a.wimg = wimg;
+    a.rimg = rimg;
     if (split6 > 0) {
       a.part = reinterpret_cast<float*>(ws + layer_workspace_fp6(M, N, K, block, n_select) - split6);
       a.ksplit = tile6_gemm_splits(M, N, K);

@@ -17,14 +17,13 @@ namespace {
 // fields 8(t%4) .. +7 (48 bits at bit 48(t%4) of lane m%32 + 32h's six
 // dwords); lanes t and t^1 pair their 48-bit chunks and the even one writes
 // the three dwords they fill.  Tokens in [M, Mpad) get codes 0, no scale.
-__global__ __launch_bounds__(256) void act_quant_fp6_kernel(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                            int64_t ldx, uint8_t* __restrict__ aimg,
-                                                            float* __restrict__ sa, int64_t Mpad) {
-  const int64_t m = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+__device__ __forceinline__ void act_quant_fp6_body(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+                                                   uint8_t* __restrict__ aimg, float* __restrict__ sa, int64_t Mpad,
+                                                   int64_t bx, int64_t j) {
+  const int64_t m = bx * 16 + (threadIdx.x >> 4);
   const int t = threadIdx.x & 15;
   if (m >= Mpad) return;  // whole 16-lane teams leave together
   const int64_t G = K / kGroup;
-  const int64_t j = blockIdx.y;
   float f[8];
   if (m < M) {
     unpack_h8(*reinterpret_cast<const uint4*>(x + m * ldx + j * kGroup + t * 8), f);
@@ -87,9 +86,9 @@ __global__ __launch_bounds__(256) void acts_fp6_kernel(const uint8_t* __restrict
 
 // Base weight codes in the slab layout (row n, group j, codes 32c .. 32c+31
 // at qw + (n/16)*8K + j*1024 + (16c + n%16)*16) -> image.
-__global__ __launch_bounds__(256) void weights_fp6_kernel(const uint8_t* __restrict__ qw, int64_t K,
-                                                          uint8_t* __restrict__ wimg, int64_t total) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void weights_fp6_body(const uint8_t* __restrict__ qw, int64_t K, uint8_t* __restrict__ wimg,
+                                                 int64_t total, int64_t bx) {
+  const int64_t i = bx * 256 + threadIdx.x;
   if (i >= total) return;
   const int64_t G = K / kGroup;
   const int l = (int)(i & 63);
@@ -105,9 +104,9 @@ __global__ __launch_bounds__(256) void weights_fp6_kernel(const uint8_t* __restr
 // Residual blocks (row r of block e: b/2 bytes at qr + (e*b + r)*(b/2)) ->
 // image: one thread per (block, piece, lane); piece p = c*(b/64) + u covers
 // rows 32c .. 32c+31 and codes 64u .. 64u+63 of the block.
-__global__ __launch_bounds__(256) void residual_fp6_kernel(const uint8_t* __restrict__ qr, int b,
-                                                           uint8_t* __restrict__ rimg, int64_t total) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void residual_fp6_body(const uint8_t* __restrict__ qr, int b, uint8_t* __restrict__ rimg,
+                                                  int64_t total, int64_t bx) {
+  const int64_t i = bx * 256 + threadIdx.x;
   if (i >= total) return;
   const int l = (int)(i & 63);
   const int np = (b / 32) * (b / 64);  // pieces per block
@@ -125,13 +124,69 @@ __global__ __launch_bounds__(256) void residual_fp6_kernel(const uint8_t* __rest
   *reinterpret_cast<uint2*>(piece + 1024 + 8 * l) = make_uint2(d[4], d[5]);
 }
 
+__global__ __launch_bounds__(256) void weights_fp6_kernel(const uint8_t* __restrict__ qw, int64_t K,
+                                                          uint8_t* __restrict__ wimg, int64_t total) {
+  weights_fp6_body(qw, K, wimg, total, blockIdx.x);
+}
+__global__ __launch_bounds__(256) void residual_fp6_kernel(const uint8_t* __restrict__ qr, int b,
+                                                           uint8_t* __restrict__ rimg, int64_t total) {
+  residual_fp6_body(qr, b, rimg, total, blockIdx.x);
+}
+
+// The fp6 layer's three preparations in one launch: blocks [0, na) quantise
+// the activations, the next nw convert the base, the rest the residual
+// blocks.  They are independent and bound by memory traffic; one grid lets
+// them share the machine instead of running back to back.
+struct Fp6Prep {
+  const uint16_t* x;
+  int64_t M, K, ldx, Mpad;
+  uint8_t* aimg;
+  float* sa;
+  const uint8_t* qw;
+  uint8_t* wimg;
+  int64_t wtotal;
+  const uint8_t* qr;
+  int block;
+  uint8_t* rimg;
+  int64_t rtotal;
+  int64_t na_x, na, nw;  // act-quant grid width (Mpad/16), act-quant blocks, base blocks
+};
+__global__ __launch_bounds__(256) void fp6_prep_kernel(Fp6Prep p) {
+  const int64_t b = blockIdx.x;
+  if (b < p.na) {
+    act_quant_fp6_body(p.x, p.M, p.K, p.ldx, p.aimg, p.sa, p.Mpad, b % p.na_x, b / p.na_x);
+  } else if (b < p.na + p.nw) {
+    weights_fp6_body(p.qw, p.K, p.wimg, p.wtotal, b - p.na);
+  } else {
+    residual_fp6_body(p.qr, p.block, p.rimg, p.rtotal, b - p.na - p.nw);
+  }
+}
+
 }  // namespace
 
-hipError_t launch_act_quant_fp6(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* aimg,
-                                float* sa, hipStream_t st) {
-  const int64_t Mpad = wide_rows(M);
-  hipLaunchKernelGGL(act_quant_fp6_kernel, dim3((unsigned)(Mpad / 16), (unsigned)(K / kGroup)), dim3(256), 0,
-                     st, x, M, K, ldx, aimg, sa, Mpad);
+hipError_t launch_fp6_layer_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* aimg, float* sa,
+                                 const uint8_t* qw, int64_t N, uint8_t* wimg, const uint8_t* qr, int n_select,
+                                 int block, uint8_t* rimg, hipStream_t st) {
+  Fp6Prep p;
+  p.x = x;
+  p.M = M;
+  p.K = K;
+  p.ldx = ldx;
+  p.Mpad = wide_rows(M);
+  p.aimg = aimg;
+  p.sa = sa;
+  p.qw = qw;
+  p.wimg = wimg;
+  p.wtotal = N / 32 * (K / kGroup) * 128;
+  p.qr = qr;
+  p.block = block;
+  p.rimg = rimg;
+  p.rtotal = n_select > 0 ? (int64_t)n_select * (block / 32) * (block / 64) * 64 : 0;
+  p.na_x = p.Mpad / 16;
+  p.na = p.na_x * (K / kGroup);
+  p.nw = (p.wtotal + 255) / 256;
+  const int64_t nr = (p.rtotal + 255) / 256;
+  hipLaunchKernelGGL(fp6_prep_kernel, dim3((unsigned)(p.na + p.nw + nr)), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 

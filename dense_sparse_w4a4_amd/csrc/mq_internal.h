@@ -303,11 +303,13 @@ hipError_t launch_widen_acts(const uint8_t* qa, int64_t M, int64_t K, uint8_t* q
 // 1024 + 8 l of the piece.
 inline size_t fp6_rows_bytes(int64_t rows, int64_t K) { return (size_t)((rows + 31) / 32) * (size_t)(K / kGroup) * kFp6Frag; }
 inline size_t fp6_residual_bytes(int64_t n_select, int block) { return (size_t)n_select * (size_t)block * block * 3 / 4; }
-hipError_t launch_act_quant_fp6(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* aimg,
-                                float* sa, hipStream_t st);
 hipError_t launch_acts_fp6(const uint8_t* qa, int64_t M, int64_t K, uint8_t* aimg, hipStream_t st);
 hipError_t launch_weights_fp6(const uint8_t* qw, int64_t N, int64_t K, uint8_t* wimg, hipStream_t st);
 hipError_t launch_residual_fp6(const uint8_t* qr, int n_select, int block, uint8_t* rimg, hipStream_t st);
+// act-quant into the activation image, base and residual conversion, in one launch
+hipError_t launch_fp6_layer_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* aimg, float* sa,
+                                 const uint8_t* qw, int64_t N, uint8_t* wimg, const uint8_t* qr, int n_select,
+                                 int block, uint8_t* rimg, hipStream_t st);
 bool tile6_gemm_fits(const GemmArgs& a);
 int tile6_gemm_splits(int64_t M, int64_t N, int64_t K);  // K splits of the fp6 route
 hipError_t launch_tile6_gemm(const GemmArgs& a, hipStream_t st);
