@@ -797,9 +797,10 @@ mq_status mq_fp6_sizes(int64_t M, int64_t N, int64_t K, int32_t block, int32_t n
 
 mq_status mq_fp6_prepare_acts(const uint8_t* qa, int64_t M, int64_t K, uint8_t* act_img, void* stream) {
   g_err[0] = 0;
-  MQ_REQUIRE(M >= 0 && M < ((int64_t)1 << 31) && M * K < ((int64_t)1 << 32), MQ_ERR_SHAPE, "bad M");
   MQ_REQUIRE(K > 0 && K % kGroup == 0 && K < ((int64_t)1 << 31), MQ_ERR_SHAPE,
-             "K = %lld must be a positive multiple of 128", (long long)K);
+             "K = %lld must be a positive multiple of 128 below 2^31", (long long)K);
+  MQ_REQUIRE(M >= 0 && M < ((int64_t)1 << 31) && M * K < ((int64_t)1 << 32), MQ_ERR_SHAPE,
+             "M = %lld: M must be in [0, 2^31) and M*K below 2^32", (long long)M);
   if (M == 0) return MQ_OK;
   MQ_REQUIRE(qa && act_img, MQ_ERR_NULL_PTR, "qa and act_img must be non-NULL");
   MQ_REQUIRE(aligned16(qa) && aligned16(act_img), MQ_ERR_ALIGN, "device pointers must be 16-byte aligned");

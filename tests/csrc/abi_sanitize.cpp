@@ -14,9 +14,10 @@
 
 static int calls = 0, fails = 0;
 
-static void expect(const char* what, int line, mq_status got, int want0, int want1 = -1, int want2 = -1) {
+static void expect(const char* what, int line, mq_status got, int want0, int want1 = -1, int want2 = -1,
+                   int want3 = -1) {
   ++calls;
-  if (got != want0 && got != want1 && got != want2) {
+  if (got != want0 && got != want1 && got != want2 && got != want3) {
     printf("FAIL %s (line %d): status %d, detail: %s\n", what, line, (int)got, mq_last_error());
     ++fails;
   }
@@ -53,6 +54,15 @@ int main() {
           EXPECT(mq_distortion_workspace(N, K, T, b, &bytes), OK, SHAPE, BLOCK);
         }
   EXPECT(mq_fused_gemm_workspace(16, 4096, 4096, nullptr), MQ_ERR_NULL_PTR);
+  // the fp6 route's size query: OK, a shape, block or budget error, never UB
+  size_t ab = 0, wb = 0, pb = 0;
+  for (int64_t M : sizes)
+    for (int64_t N : sizes)
+      for (int64_t K : sizes)
+        for (int32_t b : blocks)
+          for (int32_t ns : {0, 1, INT32_MAX})
+            EXPECT(mq_fp6_sizes(M, N, K, b, ns, &ab, &wb, &pb), OK, SHAPE, BLOCK, MQ_ERR_BUDGET);
+  EXPECT(mq_fp6_sizes(4096, 4096, 4096, 64, 0, nullptr, &wb, &pb), MQ_ERR_NULL_PTR);
 
   // entry points with extreme sizes: rejected before any device work (the
   // other arguments are otherwise valid-looking, so the size checks are
@@ -92,6 +102,17 @@ int main() {
                                   (size_t)1 << 40, nullptr), SHAPE);
     EXPECT(mq_distortion(P16, P16, 4096, big, 64, 64, P32, 1, PD, PV, (size_t)1 << 40, nullptr), SHAPE);
     EXPECT(mq_validate_csr(P32, P32, big, 4096, 64, 1, nullptr), SHAPE, MQ_ERR_CSR);
+    // the fp6 route's preparation and GEMM: every extreme size rejected
+    EXPECT(mq_fp6_prepare_acts(P8, big, 4096, P8, nullptr), SHAPE);
+    EXPECT(mq_fp6_prepare_acts(P8, 4096, big, P8, nullptr), SHAPE);
+    EXPECT(mq_fp6_prepare_weights(P8, big, 4096, 64, 1, P8, P8, nullptr), SHAPE);
+    EXPECT(mq_fp6_prepare_weights(P8, 4096, big, 64, 1, P8, P8, nullptr), SHAPE);
+    EXPECT(mq_fused_gemm_fp6(P8, PF, big, 4096, 4096, P8, P16, 64, 1, P32, P32, P16, P16, 4096, nullptr, 0, 0,
+                             nullptr, nullptr), SHAPE);
+    EXPECT(mq_fused_gemm_fp6(P8, PF, 4096, big, 4096, P8, P16, 64, 1, P32, P32, P16, P16, 4096, nullptr, 0, 0,
+                             nullptr, nullptr), SHAPE);
+    EXPECT(mq_fused_gemm_fp6(P8, PF, 4096, 4096, big, P8, P16, 64, 1, P32, P32, P16, P16, 4096, nullptr, 0, 0,
+                             nullptr, nullptr), SHAPE);
   }
 
   // budgets, blocks, null and misaligned pointers
@@ -101,6 +122,21 @@ int main() {
     EXPECT(mq_fused_layer(P16, 16, 4096, 4096, 4096, P8, P16, b, 1, P32, P32, P8, P16, P16, 4096, nullptr, 0,
                           nullptr), BLOCK);
   }
+  for (int32_t b : blocks) {
+    if (b == 64 || b == 128) continue;
+    EXPECT(mq_fp6_prepare_weights(P8, 4096, 4096, b, 1, P8, P8, nullptr), BLOCK);
+    EXPECT(mq_fused_gemm_fp6(P8, PF, 4096, 4096, 4096, P8, P16, b, 1, P32, P32, P16, P16, 4096, nullptr, 0, 0,
+                             nullptr, nullptr), BLOCK);
+  }
+  for (int32_t ns : {INT32_MIN, -1, 4097, INT32_MAX}) {
+    EXPECT(mq_fp6_prepare_weights(P8, 4096, 4096, 64, ns, P8, P8, nullptr), MQ_ERR_BUDGET);
+    EXPECT(mq_fused_gemm_fp6(P8, PF, 4096, 4096, 4096, P8, P16, 64, ns, P32, P32, P16, P16, 4096, nullptr, 0, 0,
+                             nullptr, nullptr), MQ_ERR_BUDGET);
+  }
+  EXPECT(mq_fused_gemm_fp6(P8, PF, 16, 4096, 4096, P8, P16, 64, 1, P32, P32, P16, P16, 4096, nullptr, 0, 0,
+                           nullptr, nullptr), SHAPE);  // M <= 32
+  EXPECT(mq_fused_gemm_fp6(P8, PF, 4096, 4096, 4096, P8, P16, 64, 1, P32, P32, P16, PM16, 4096, nullptr, 0, 0,
+                           nullptr, nullptr), MQ_ERR_ALIGN);
   for (int32_t ns : {INT32_MIN, -1, 4097, INT32_MAX}) {
     EXPECT(mq_select_blocks(P16, P16, 4096, 4096, 64, 64, ns, P32, PD, PD, nullptr), MQ_ERR_BUDGET);
     EXPECT(mq_fused_gemm(P8, PF, 16, 4096, 4096, P8, P16, 64, ns, P32, P32, P8, P16, P16, 4096, nullptr, 0, 0,
