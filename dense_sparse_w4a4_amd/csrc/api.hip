@@ -418,15 +418,19 @@ static size_t layer_workspace_i8(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K < kGroup || stream_quant_fits(M, N, K)) return 0;
   return layer_codes_bytes(M, K) + round256((size_t)M * (size_t)(K / kGroup) * 4) + split_workspace(M, N, K);
 }
-// The fp6 route: the activation scales, the fp6 images, the split-K partials.
-static size_t layer_scales_bytes(int64_t M, int64_t K) { return round256((size_t)M * (size_t)(K / kGroup) * 4); }
+// The fp6 route: the activation scales group-major [K/128][wide_rows(M)]
+// (fp32) and the weight scales group-major [K/128][N] (fp16), the fp6
+// images, the split-K partials.
+static size_t layer_scales_bytes(int64_t M, int64_t N, int64_t K) {
+  return round256((size_t)wide_rows(M) * (size_t)(K / kGroup) * 4) + round256((size_t)N * (size_t)(K / kGroup) * 2);
+}
 static size_t layer_workspace_fp6(int64_t M, int64_t N, int64_t K, int block, int64_t n_select) {
-  return layer_scales_bytes(M, K) + fp6_images_bytes(M, N, K, block, n_select) + split6_workspace(M, N, K);
+  return layer_scales_bytes(M, N, K) + fp6_images_bytes(M, N, K, block, n_select) + split6_workspace(M, N, K);
 }
 static size_t layer_workspace(int64_t M, int64_t N, int64_t K) {
   const size_t i8 = layer_workspace_i8(M, N, K);
   if (M < kFp6MinM || N <= 0 || K < kGroup) return i8;
-  const size_t f6 = layer_scales_bytes(M, K) + fp6_images_bound(M, N, K) + split6_workspace(M, N, K);
+  const size_t f6 = layer_scales_bytes(M, N, K) + fp6_images_bound(M, N, K) + split6_workspace(M, N, K);
   return i8 > f6 ? i8 : f6;
 }
 
@@ -520,20 +524,24 @@ static mq_status layer_run(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
   const size_t split = split_workspace(M, N, K);
   const size_t split6 = split6_workspace(M, N, K);
   if (M >= kFp6MinM && tile6_gemm_fits(a) && ws_bytes >= layer_workspace_fp6(M, N, K, block, n_select)) {
-    // fp6 tile kernel: scales, then the images (act-quant into the
-    // activation image and the base and residual conversions in one launch)
-    float* sa6 = reinterpret_cast<float*>(ws);
-    a.sa = sa6;
-    uint8_t* aimg = ws + layer_scales_bytes(M, K);
+    // fp6 tile kernel: the group-major scales, then the images (act-quant
+    // into the activation image and the base and residual conversions in
+    // one launch)
+    float* saT = reinterpret_cast<float*>(ws);
+    uint16_t* swT = reinterpret_cast<uint16_t*>(ws + round256((size_t)wide_rows(M) * (size_t)(K / kGroup) * 4));
+    uint8_t* aimg = ws + layer_scales_bytes(M, N, K);
     uint8_t* wimg = aimg + round256(fp6_rows_bytes(M, K));
     uint8_t* rimg = wimg + round256(fp6_rows_bytes(N, K));
-    const mq_status s = hip_status(launch_fp6_layer_prep(x, M, K, ldx, aimg, sa6, qw, N, wimg, a.qr, n_select,
-                                                         block, rimg, st),
+    const mq_status s = hip_status(launch_fp6_layer_prep(x, M, K, ldx, aimg, saT, qw, sw, N, wimg, swT, a.qr,
+                                                         n_select, block, rimg, st),
                                    "mq_fused_layer fp6 preparation launch");
     if (s != MQ_OK) return s;
     a.aimg = aimg;
     a.wimg = wimg;
     a.rimg = rimg;
+    a.saT = saT;
+    a.swT = swT;
+    a.saT_ld = wide_rows(M);
     if (split6 > 0) {
       a.part = reinterpret_cast<float*>(ws + layer_workspace_fp6(M, N, K, block, n_select) - split6);
       a.ksplit = tile6_gemm_splits(M, N, K);

@@ -12,13 +12,14 @@ namespace mq {
 namespace {
 
 // Activation quantisation straight into the FP6 image: one 16-lane team per
-// (token, group), 16 consecutive tokens of one group per workgroup.  Lane t
+// (token, group), 16 consecutive tokens of one group per workgroup; the
+// scales group-major ([K/128][Mpad]).  Lane t
 // quantises channels 8t .. 8t+7, i.e. slice u = t/8, half h = (t/4)%2,
 // fields 8(t%4) .. +7 (48 bits at bit 48(t%4) of lane m%32 + 32h's six
 // dwords); lanes t and t^1 pair their 48-bit chunks and the even one writes
 // the three dwords they fill.  Tokens in [M, Mpad) get codes 0, no scale.
 __device__ __forceinline__ void act_quant_fp6_body(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                                                   uint8_t* __restrict__ aimg, float* __restrict__ sa, int64_t Mpad,
+                                                   uint8_t* __restrict__ aimg, float* __restrict__ saT, int64_t Mpad,
                                                    int64_t bx, int64_t j) {
   const int64_t m = bx * 16 + (threadIdx.x >> 4);
   const int t = threadIdx.x & 15;
@@ -56,7 +57,7 @@ __device__ __forceinline__ void act_quant_fp6_body(const uint16_t* __restrict__ 
       *reinterpret_cast<uint2*>(img + fp6_hi_offset(u, l)) = make_uint2(d1, d2);
     }
   }
-  if (t == 0 && m < M) sa[m * G + j] = s;
+  if (t == 0) saT[j * Mpad + m] = s;  // group-major; padding rows get 0
 }
 
 // A lane's 32 codes (four packed words) -> its two pieces of slice u.
@@ -143,7 +144,10 @@ struct Fp6Prep {
   uint8_t* aimg;
   float* sa;
   const uint8_t* qw;
+  const uint16_t* sw;
+  int64_t N;
   uint8_t* wimg;
+  uint16_t* swT;
   int64_t wtotal;
   const uint8_t* qr;
   int block;
@@ -156,7 +160,17 @@ __global__ __launch_bounds__(256) void fp6_prep_kernel(Fp6Prep p) {
   if (b < p.na) {
     act_quant_fp6_body(p.x, p.M, p.K, p.ldx, p.aimg, p.sa, p.Mpad, b % p.na_x, b / p.na_x);
   } else if (b < p.na + p.nw) {
-    weights_fp6_body(p.qw, p.K, p.wimg, p.wtotal, b - p.na);
+    const int64_t bw = b - p.na;
+    weights_fp6_body(p.qw, p.K, p.wimg, p.wtotal, bw);
+    // the weight scales group-major: the thread of (column block cb, group j,
+    // slice 0, lane l < 32) copies sw[n][j], n = 32 cb + l
+    const int64_t i = bw * 256 + threadIdx.x;
+    const int l = (int)(i & 63);
+    if (i < p.wtotal && ((i >> 6) & 1) == 0 && l < 32) {
+      const int64_t G = p.K / kGroup, bj = i >> 7;
+      const int64_t cb = bj / G, j = bj - cb * G, n = cb * 32 + l;
+      p.swT[j * p.N + n] = p.sw[n * G + j];
+    }
   } else {
     residual_fp6_body(p.qr, p.block, p.rimg, p.rtotal, b - p.na - p.nw);
   }
@@ -164,9 +178,9 @@ __global__ __launch_bounds__(256) void fp6_prep_kernel(Fp6Prep p) {
 
 }  // namespace
 
-hipError_t launch_fp6_layer_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* aimg, float* sa,
-                                 const uint8_t* qw, int64_t N, uint8_t* wimg, const uint8_t* qr, int n_select,
-                                 int block, uint8_t* rimg, hipStream_t st) {
+hipError_t launch_fp6_layer_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* aimg, float* saT,
+                                 const uint8_t* qw, const uint16_t* sw, int64_t N, uint8_t* wimg, uint16_t* swT,
+                                 const uint8_t* qr, int n_select, int block, uint8_t* rimg, hipStream_t st) {
   Fp6Prep p;
   p.x = x;
   p.M = M;
@@ -174,9 +188,12 @@ hipError_t launch_fp6_layer_prep(const uint16_t* x, int64_t M, int64_t K, int64_
   p.ldx = ldx;
   p.Mpad = wide_rows(M);
   p.aimg = aimg;
-  p.sa = sa;
+  p.sa = saT;
   p.qw = qw;
+  p.sw = sw;
+  p.N = N;
   p.wimg = wimg;
+  p.swT = swT;
   p.wtotal = N / 32 * (K / kGroup) * 128;
   p.qr = qr;
   p.block = block;

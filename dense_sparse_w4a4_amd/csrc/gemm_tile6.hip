@@ -257,15 +257,24 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
     baseS = ((rp_row[rb] - 1) * BLK + (int)(n - (int64_t)(nt0 + rb) * BLK)) * 2;
     slotS = (uint32_t)(C::SR_OFF + (((r >> 5) * C::NBC + c) * 32 + (r & 31)) * 8);
   }
-  const uint32_t offS = wave < 4 ? (uint32_t)(min(m0 + tid, a.M - 1) * G * 4)
-                                 : (uint32_t)(min(n0 + min(tid - 256, TBN - 1), a.N - 1) * G * 2);
+  // scale of this lane for group 0 and the step to the next group: waves 0-3
+  // token m0 + tid's sa, waves 4-7 channel n0 + tid - 256's sw (past the
+  // end: the last one), group-major when the caller gives saT / swT (one
+  // contiguous run per group), else [M][G] / [N][G]
+  const int64_t msc = wave < 4 ? min(m0 + tid, (a.saT ? a.saT_ld : a.M) - 1) : 0;
+  const int64_t nsc = min(n0 + min(tid - 256, TBN - 1), a.N - 1);
+  const uint8_t* scb = wave < 4 ? (a.saT ? reinterpret_cast<const uint8_t*>(a.saT) + msc * 4
+                                         : reinterpret_cast<const uint8_t*>(a.sa) + msc * G * 4)
+                                : (a.swT ? reinterpret_cast<const uint8_t*>(a.swT) + nsc * 2
+                                         : reinterpret_cast<const uint8_t*>(a.sw) + nsc * G * 2);
+  const int64_t sc_step = wave < 4 ? (a.saT ? a.saT_ld * 4 : 4) : (a.swT ? a.N * 2 : 2);
 
   auto load = [&](Stage6& S, int j) {
     j = min(j, je - 1);
     if (wave < 4) {
-      S.sc = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const uint8_t*>(a.sa) + j * 4 + offS);
+      S.sc = *reinterpret_cast<const uint32_t*>(scb + j * sc_step);
     } else {
-      S.sc = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(a.sw) + j * 2 + offS);
+      S.sc = *reinterpret_cast<const uint16_t*>(scb + j * sc_step);
     }
     // residual pieces and row scales: loaded in every step, from offset 0 of
     // a valid buffer where no block is selected, so the DMA wait is exact

@@ -256,6 +256,12 @@ struct GemmArgs {
   const uint8_t* aimg;
   const uint8_t* wimg;
   const uint8_t* rimg;
+  // fp6 route, optional: the scales group-major (saT [K/128][saT_ld] fp32,
+  // swT [K/128][N] fp16), so that a tile's scales of one group are one
+  // contiguous run; null: sa [M][K/128], sw [N][K/128]
+  const float* saT;
+  const uint16_t* swT;
+  int64_t saT_ld;
 };
 
 // In-kernel activation quantisation of the streaming kernel: at most
@@ -307,9 +313,11 @@ hipError_t launch_acts_fp6(const uint8_t* qa, int64_t M, int64_t K, uint8_t* aim
 hipError_t launch_weights_fp6(const uint8_t* qw, int64_t N, int64_t K, uint8_t* wimg, hipStream_t st);
 hipError_t launch_residual_fp6(const uint8_t* qr, int n_select, int block, uint8_t* rimg, hipStream_t st);
 // act-quant into the activation image, base and residual conversion, in one launch
-hipError_t launch_fp6_layer_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* aimg, float* sa,
-                                 const uint8_t* qw, int64_t N, uint8_t* wimg, const uint8_t* qr, int n_select,
-                                 int block, uint8_t* rimg, hipStream_t st);
+// (the activation scales written group-major, saT [K/128][wide_rows(M)];
+// the weight scales sw [N][K/128] copied group-major into swT [K/128][N])
+hipError_t launch_fp6_layer_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* aimg, float* saT,
+                                 const uint8_t* qw, const uint16_t* sw, int64_t N, uint8_t* wimg, uint16_t* swT,
+                                 const uint8_t* qr, int n_select, int block, uint8_t* rimg, hipStream_t st);
 bool tile6_gemm_fits(const GemmArgs& a);
 int tile6_gemm_splits(int64_t M, int64_t N, int64_t K);  // K splits of the fp6 route
 hipError_t launch_tile6_gemm(const GemmArgs& a, hipStream_t st);
