@@ -590,16 +590,22 @@ def main():
             (_, _, L0, x, qa, sa, y, ws, gws, f6) = sets[0][p_idx]
             n = max(2, -(-ROTATE_BYTES // L0.nbytes()))
             copies = [L0.clone() for _ in range(n)]
+            # pairs on the int8 tile route: also the fp6 kernel on prepared
+            # images (a deployment that keeps the converted weights)
+            p6 = None
+            if f6 is None and kern[p_idx] == "gemm_tile_kernel" and spec.block in (64, 128):
+                _, _, pb = ops.fp6_sizes(M, spec.N, spec.K, spec.block, spec.n_select)
+                p6 = (ops.fp6_prepare_acts(qa, spec.K), torch.empty(max(pb, 1), dtype=torch.uint8, device=dev))
             # the fp6 kernel reads prepared images: one per copy, so its
             # launches rotate through as many weight bytes as the others
-            imgs = [ops.fp6_prepare_weights(L) for L in copies] if f6 is not None else None
+            imgs = [ops.fp6_prepare_weights(L) for L in copies] if (f6 is not None or p6 is not None) else None
             if f6 is not None:
                 dimgs = [ops.fp6_prepare_weights(ops.PackedLayer(L.N, L.K, L.block, L.qw, L.sw,
                                                                  torch.zeros_like(L.row_ptr), L.col_idx[:0],
                                                                  L.qr[:0], L.sr[:0])) for L in copies]
             q2, s2 = torch.empty_like(qa), torch.empty_like(sa)
             res = {}
-            for mode in modes:
+            for mode in modes + (["fp6_prepared"] if p6 is not None else []):
                 g = torch.cuda.CUDAGraph()
                 with torch.cuda.graph(g, stream=cap):
                     for ci, L in enumerate(copies):
@@ -609,6 +615,8 @@ def main():
                             ops.fused_layer(x, L, out=y, workspace=ws)
                         elif mode == "actq":
                             ops.quantize_act(x, q2, s2)
+                        elif mode == "fp6_prepared":
+                            ops.fused_gemm_fp6(p6[0], sa, M, L, imgs[ci], out=y, split_ws=p6[1])
                         elif f6 is not None and mode in ("fused", "dense"):
                             ops.fused_gemm_fp6(f6[0], sa, M, L if mode == "fused" else D,
                                                imgs[ci] if mode == "fused" else dimgs[ci], out=y,
@@ -629,7 +637,7 @@ def main():
                     samples.append(e0.elapsed_time(e1) * 1e3 / n)
                 res[mode] = samples
                 del g
-            del copies, imgs
+            del copies, imgs, p6
             if f6 is not None:
                 del dimgs
             torch.cuda.empty_cache()
@@ -650,6 +658,8 @@ def main():
                        act_quant_us_p50=round(med["actq"], 3),
                        layer_us_p50=round(med["layer"], 3), layer_one_kernel=bool(one_kernel[p_idx]),
                        samples=PAIR_REPLAYS, copies=n)
+            if "fp6_prepared" in med:
+                row["fp6_prepared_us_p50"] = round(med["fp6_prepared"], 3)
             if "unfused" in med:
                 row["unfused_us_p50"] = round(med["unfused"], 3)
                 row["unfused_over_fused"] = round(med["unfused"] / med["fused"], 4)
@@ -660,7 +670,8 @@ def main():
                 f"{'fp6' if kern[p_idx] == 'gemm_tile6_kernel' else 'int8'} peak, {row['frac_int8_peak']:5.1%} int8)  "
                 f"dense-only {med['dense']:9.2f} us (residual +{row['residual_cost']:5.1%})  "
                 f"act-quant {med['actq']:7.2f} us  layer {med['layer']:9.2f} us"
-                + (f"  unfused x{row['unfused_over_fused']:.3f}" if "unfused" in med else ""))
+                + (f"  unfused x{row['unfused_over_fused']:.3f}" if "unfused" in med else "")
+                + (f"  fp6 on prepared images {row['fp6_prepared_us_p50']:.2f} us" if "fp6_prepared" in med else ""))
 
     # ---- rooflines: each kernel's algorithmic work per launch over its
     # average launch time; the dominant kernel (most time per step) first ----
