@@ -34,10 +34,13 @@
 // the same bf16 split, scaled by powers of two), so the two routes give the
 // same fp32 partial sums and the same fp16 outputs.
 //
-// Pipeline, residual table, split-K and work order as in gemm_tile.hip: two
-// LDS stages, one LDS-only barrier per group, register buffers two groups
-// ahead, every step issuing the same loads (dummy offsets where no residual
-// block is selected) so that the DMA wait counts them exactly.
+// Pipeline and residual table as in gemm_tile.hip: two LDS stages, one
+// LDS-only barrier per group, register buffers two groups ahead, every step
+// issuing the same loads (dummy offsets where no residual block is selected)
+// so that the DMA wait counts them exactly.  Work order: banded and
+// XCD-aware as there, but K is split only for the tiles of a partial last
+// round (all tiles when there are fewer than one round), the others taking
+// all of K first, so the partials' HBM round trip covers only those tiles.
 #include "gemm_common.h"
 
 namespace mq {
@@ -52,6 +55,17 @@ constexpr int TBM = 256;
 constexpr int TBN = 128;
 constexpr int NTHR = 512;
 constexpr size_t kMaxLds = 160 * 1024;
+
+// Origin of tile t in the banded order: bands of four token tiles, channel
+// tiles outer within a band, so that consecutive tiles share weight tiles.
+__device__ __forceinline__ void tile6_origin(int t, int tiles_m, int tiles_n, int64_t& m0, int64_t& n0) {
+  constexpr int kBand = 4;
+  const int band = t / (kBand * tiles_n);
+  const int bh = min(kBand, tiles_m - band * kBand);
+  const int rbi = t - band * kBand * tiles_n;
+  m0 = (int64_t)(band * kBand + rbi % bh) * TBM;
+  n0 = (int64_t)(rbi / bh) * TBN;
+}
 
 template <int BLK>
 struct Tile6Cfg {
@@ -147,24 +161,35 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6) & 7;
   const int lane = tid & 63;
 
-  // work order: XCD-aware, banded, split-K as in the int8 route
+  // work order: the first `full` tiles (banded order) take all of K, the
+  // last `tail` tiles are split ksplit ways (tail = every tile: split-K as in
+  // the int8 route).  Workgroup b runs on XCD b % 8; each XCD takes a
+  // contiguous share of the full tiles and then a contiguous share of the
+  // split units, so the short units fill the last round everywhere.
   const int tiles_n = (int)((a.N + TBN - 1) / TBN);
-  const int items = (int)gridDim.x;
-  const int tiles = items / a.ksplit;
-  const int xcd = blockIdx.x % 8;
-  const int per = items / 8, rem = items % 8;
-  const int item = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + blockIdx.x / 8;
-  const int split = item / tiles;
-  const int tile = item - split * tiles;
-  const int jb = (int)((int64_t)split * G / a.ksplit);
-  const int je = (int)((int64_t)(split + 1) * G / a.ksplit);
-  constexpr int kBand = 4;
-  const int tiles_m = tiles / tiles_n;
-  const int band = tile / (kBand * tiles_n);
-  const int bh = min(kBand, tiles_m - band * kBand);
-  const int rbi = tile - band * kBand * tiles_n;
-  const int64_t m0 = (int64_t)(band * kBand + rbi % bh) * TBM;
-  const int64_t n0 = (int64_t)(rbi / bh) * TBN;
+  const int tiles_m = (int)((a.M + TBM - 1) / TBM);
+  const int tiles = tiles_m * tiles_n;
+  const int tail = a.ksplit > 1 ? a.split_tail : 0;
+  const int full = tiles - tail;
+  const int items = (int)gridDim.x;  // full + tail * ksplit
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int nfull = full / 8 + (xcd < full % 8 ? 1 : 0);
+  const int fbase = xcd * (full / 8) + min(xcd, full % 8);
+  int tile, split, jb, je;
+  if (slot < nfull) {
+    tile = fbase + slot;
+    split = -1;
+    jb = 0;
+    je = G;
+  } else {
+    const int unit = xcd * (items / 8) + min(xcd, items % 8) - fbase + (slot - nfull);
+    split = unit / tail;
+    tile = full + (unit - split * tail);
+    jb = (int)((int64_t)split * G / a.ksplit);
+    je = (int)((int64_t)(split + 1) * G / a.ksplit);
+  }
+  int64_t m0, n0;
+  tile6_origin(tile, tiles_m, tiles_n, m0, n0);
   const int nt0 = (int)(n0 / BLK);
   const int nrows_b = (int)(a.N / BLK);
 
@@ -466,7 +491,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
       for (int e = 0; e < 16; ++e) {
         const int64_t m = m0 + (wm * 2 + rb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         if (m < a.M && n < a.N) {
-          if (a.part)
+          if (split >= 0)
             a.part[((int64_t)split * a.M + m) * a.N + n] = y[rb][cb][e];
           else
             a.y[m * a.ldy + n] = f2h_bits(y[rb][cb][e]);
@@ -475,14 +500,18 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
     }
 }
 
-// Split-K reduce: y = fp16(sum of the splits' fp32 partials, in split order),
-// four consecutive outputs per thread (N is a multiple of 32): 16-byte
-// partial loads, one 8-byte store.
+// Split-K reduce over the split tiles only: y = fp16(sum of the splits' fp32
+// partials, in split order).  32 workgroups per tile, four consecutive
+// outputs per thread (N is a multiple of 32): 16-byte partial loads, one
+// 8-byte store.
 __global__ __launch_bounds__(256) void split_reduce6_kernel(const float* __restrict__ part, int ksplit, int64_t M,
-                                                            int64_t N, uint16_t* y, int64_t ldy) {
-  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
-  if (idx >= M * N) return;
-  const int64_t m = idx / N, n = idx - m * N;
+                                                            int64_t N, uint16_t* y, int64_t ldy, int full) {
+  const int tiles_n = (int)((N + TBN - 1) / TBN), tiles_m = (int)((M + TBM - 1) / TBM);
+  int64_t m0, n0;
+  tile6_origin(full + (int)(blockIdx.x / 32), tiles_m, tiles_n, m0, n0);
+  const int e = ((int)(blockIdx.x % 32) * 256 + (int)threadIdx.x) * 4;  // < TBM * TBN
+  const int64_t m = m0 + e / TBN, n = n0 + e % TBN;
+  if (m >= M || n >= N) return;
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int k = 0; k < ksplit; ++k) {
     const float4 v = *reinterpret_cast<const float4*>(part + ((int64_t)k * M + m) * N + n);
@@ -505,39 +534,83 @@ hipError_t launch_tile6_cfg(const GemmArgs& a, hipStream_t st) {
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t tiles = ((a.M + TBM - 1) / TBM) * ((a.N + TBN - 1) / TBN);
-  hipLaunchKernelGGL(kern, dim3((unsigned)(tiles * a.ksplit)), dim3(NTHR), lds, st, a);
+  GemmArgs b = a;
+  b.split_tail = a.ksplit > 1 ? (int)tile6_gemm_tail(a.M, a.N, a.K, a.ksplit) : 0;
+  if (b.ksplit > 1 && b.part == nullptr) return hipErrorInvalidValue;
+  const int64_t full = tiles - b.split_tail;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(full + (int64_t)b.split_tail * b.ksplit)), dim3(NTHR), lds, st, b);
   e = hipGetLastError();
-  if (e != hipSuccess || a.ksplit == 1) return e;
-  hipLaunchKernelGGL(split_reduce6_kernel, dim3((unsigned)((a.M * a.N / 4 + 255) / 256)), dim3(256), 0, st, a.part,
-                     a.ksplit, a.M, a.N, a.y, a.ldy);
+  if (e != hipSuccess || b.ksplit == 1) return e;
+  hipLaunchKernelGGL(split_reduce6_kernel, dim3((unsigned)(b.split_tail * 32)), dim3(256), 0, st, b.part, b.ksplit,
+                     b.M, b.N, b.y, b.ldy, (int)full);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// K splits of the fp6 route: the fewest splits within 3% of the best
-// estimate of whole rounds of one 512-thread workgroup per CU times groups
-// per workgroup (about 1.4 us per group) plus the fp32 partials' round trip
-// through HBM (written once, read once, at about 5 TB/s).  Unlike the int8
-// route's rule it also splits when the tiles leave a partial last round
-// (Qwen3-32B 25600 x 5120 at M = 4096: 640 tiles, 2.5 rounds -> 2 splits,
-// 5 rounds of half the groups), at least 8 groups per split.
+// Work plan of the fp6 route: K splits and how many tiles take them.  The
+// estimate counts rounds of one 512-thread workgroup per CU times groups per
+// workgroup (about 1.4 us per group) plus the split tiles' fp32 partials'
+// round trip through HBM (written once, read once, at about 5 TB/s).  With
+// `tail` split tiles the other tiles fill whole rounds first (full is a
+// multiple of the CU count) and the split units share what is left.  Plain
+// split-K (every tile split) is the tail = tiles case.
+namespace {
+constexpr int64_t kPlanCUs = 256;
+
+double tile6_estimate(int64_t M, int64_t N, int64_t tiles, int64_t G, int ks, int64_t tail) {
+  constexpr double kGroupSec = 1.4e-6, kHbm = 5.0e12;
+  if (ks == 1) return (double)((tiles + kPlanCUs - 1) / kPlanCUs) * (double)G * kGroupSec;
+  const int64_t full = tiles - tail, gs = (G + ks - 1) / ks;
+  const double groups = (double)(full / kPlanCUs * G) + (double)((tail * ks + kPlanCUs - 1) / kPlanCUs * gs);
+  const double outs = std::min((double)tail * TBM * TBN, (double)M * (double)N);
+  return groups * kGroupSec + (double)(ks + 1) * outs * 4.0 / kHbm;
+}
+
+// The best tail for ks splits: every tile, or all but whole rounds of tiles.
+int64_t tile6_best_tail(int64_t M, int64_t N, int64_t tiles, int64_t G, int ks, double* est) {
+  int64_t bt = tiles;
+  double best = tile6_estimate(M, N, tiles, G, ks, tiles);
+  for (int64_t full = kPlanCUs; full < tiles; full += kPlanCUs) {
+    const double t = tile6_estimate(M, N, tiles, G, ks, tiles - full);
+    if (t < best) {
+      best = t;
+      bt = tiles - full;
+    }
+  }
+  if (est) *est = best;
+  return bt;
+}
+}  // namespace
+
+// The fewest splits within 3% of the best estimate, at least 8 groups per
+// split (Qwen3-32B 25600 x 5120 at M = 4096: 640 tiles, 2.5 rounds -> 512
+// tiles over all of K in two rounds, the last 128 split two ways).
 int tile6_gemm_splits(int64_t M, int64_t N, int64_t K) {
-  constexpr double kCUs = 256.0, kGroupSec = 1.4e-6, kHbm = 5.0e12;
   const int64_t tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
   const int64_t G = K / kGroup;
   double best = 0.0;
   int bk = 1;
   for (int ks = 1; ks <= 8 && (ks == 1 || G / ks >= 8); ++ks) {
-    const double rounds = (double)((tiles * ks + (int64_t)kCUs - 1) / (int64_t)kCUs);
-    const double t = rounds * (double)((G + ks - 1) / ks) * kGroupSec +
-                     (ks > 1 ? (double)(ks + 1) * (double)M * (double)N * 4.0 / kHbm : 0.0);
+    double t = 0.0;
+    if (ks == 1)
+      t = tile6_estimate(M, N, tiles, G, 1, 0);
+    else
+      tile6_best_tail(M, N, tiles, G, ks, &t);
     if (ks == 1 || t < best * 0.97) {
       best = t;
       bk = ks;
     }
   }
   return bk;
+}
+
+// Tiles split ks ways under the plan above (the last ones in the banded
+// order); 0 for ks = 1.
+int64_t tile6_gemm_tail(int64_t M, int64_t N, int64_t K, int ks) {
+  if (ks <= 1) return 0;
+  const int64_t tiles = ((M + TBM - 1) / TBM) * ((N + TBN - 1) / TBN);
+  return tile6_best_tail(M, N, tiles, K / kGroup, ks, nullptr);
 }
 
 // The fp6 route covers blocks of 64 and 128 (a block of 32 is half a 64-code

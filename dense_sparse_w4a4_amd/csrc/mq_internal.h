@@ -243,6 +243,8 @@ struct GemmArgs {
   int32_t* acc_dump;  // non-null => dump accumulators
   float* part;        // split-K partial outputs [ksplit][M][N] (tile kernel), or null
   int ksplit;         // K splits of the tile kernel (1 = none)
+  int split_tail;     // fp6 route: the last split_tail tiles take the K splits
+                      // (set by its launcher from the plan)
   const uint16_t* x;  // fp16 activations [M][ldx] to quantise in the streaming
   int64_t ldx;        // kernel (qa, sa unused), or null
   const uint8_t* qaw; // tile kernel: activation codes in the wide fragment order
@@ -320,6 +322,7 @@ hipError_t launch_fp6_layer_prep(const uint16_t* x, int64_t M, int64_t K, int64_
                                  const uint8_t* qr, int n_select, int block, uint8_t* rimg, hipStream_t st);
 bool tile6_gemm_fits(const GemmArgs& a);
 int tile6_gemm_splits(int64_t M, int64_t N, int64_t K);  // K splits of the fp6 route
+int64_t tile6_gemm_tail(int64_t M, int64_t N, int64_t K, int ks);  // tiles it splits
 hipError_t launch_tile6_gemm(const GemmArgs& a, hipStream_t st);
 
 }  // namespace mq

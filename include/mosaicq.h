@@ -221,7 +221,8 @@ mq_status mq_select_exact_greedy(const uint16_t* w, const uint16_t* x_calib, int
  * route (see mq_fp6_sizes): the FP6 images of the activation codes, the
  * base and the residual (bounded by every block selected, 0.75*N*K bytes,
  * since block and n_select are not arguments here) and that route's
- * split-K partials.  Sizes the GEMM does not accept (each below 2^31,
+ * split-K partials (room for [splits][M][N]; that route splits only the
+ * tiles of a partial last round when the others fill whole rounds).  Sizes the GEMM does not accept (each below 2^31,
  * packed weights and activations each below 4 GiB) give MQ_ERR_SHAPE.
  */
 mq_status mq_fused_gemm_workspace(int64_t M, int64_t N, int64_t K, size_t* bytes);

@@ -138,6 +138,35 @@ def test_gemm_on_prepared_images(M, N, K, b, frac):
     assert np.array_equal(host(z6).view(np.uint16), host(y8).view(np.uint16))
 
 
+def test_split_tail_tiles():
+    # 260 tiles of 256 x 128 (M = 1024, N = 8320, 16 groups): 256 tiles take
+    # all of K in one round and the last four (channels 8192-8319 in the
+    # banded order) are split two ways, their partials summed by the reduce
+    M, N, K, b = 1024, 8320, 2048, 64
+    print(f"fp6 split tail M={M} N={N} K={K} b={b}", flush=True)
+    rng = np.random.default_rng(11)
+    qa, _, _, ref, sa_h = _codes_layer(rng, M, N, K, b, 0.05)
+    layer = ops.PackedLayer(N, K, b, dev(ref["qw"]), dev(ref["sw"]), dev(ref["row_ptr"]),
+                            dev(ref["col_idx"]), dev(ref["qr"]), dev(ref["sr"]))
+    _, _, pb = ops.fp6_sizes(M, N, K, b, len(ref["qr"]))
+    assert pb == 2 * M * N * 4  # two K splits
+    qa_d, sa = dev(oracle.pack_nibbles(qa)), dev(sa_h)
+    y6 = ops.fused_gemm_fp6(ops.fp6_prepare_acts(qa_d, K), sa, M, layer, ops.fp6_prepare_weights(layer))
+    yr = ops.fused_gemm(qa_d, sa, layer, route="fp6")
+    y8 = ops.fused_gemm(qa_d, sa, layer, route="int8")  # one K split at 260 tiles
+    torch.cuda.synchronize()
+    h6, h8 = host(y6), host(y8)
+    assert np.array_equal(host(yr).view(np.uint16), h6.view(np.uint16))
+    # the tiles over all of K: one fp32 chain on both routes
+    assert np.array_equal(h6[:, :8192].view(np.uint16), h8[:, :8192].view(np.uint16))
+    # the split tiles: two chains summed, within one fp16 rounding of the int8 route
+    assert_y_close(y6[:, 8192:], h8[:, 8192:].astype(np.float64), tol=2.0 ** -10)
+    # rows of every token tile (and the last) against the oracle
+    rows = np.r_[0:6, 250:262, 509:515, 700:704, 1018:1024]
+    y_ref, _, _ = oracle.fused_gemm(qa[rows], sa_h[rows], ref)
+    assert_y_close(y6[torch.from_numpy(rows).to(y6.device)], y_ref)
+
+
 def test_full_size_qwen3_32b_prefill_prepared():
     # the configured Qwen3-32B MLP shapes at M = 4096 (the kernel the default
     # benchmark times): prepared route against the one-call layer and the
