@@ -12,26 +12,20 @@ namespace mq {
 namespace {
 
 // Activation quantisation straight into the FP6 image: one 16-lane team per
-// (token, group), 16 consecutive tokens of one group per workgroup; the
-// scales group-major ([K/128][Mpad]).  Lane t
+// token and four consecutive groups (its four 16-byte loads issued first),
+// 16 consecutive tokens per workgroup; the scales group-major
+// ([K/128][Mpad]).  Per group, lane t
 // quantises channels 8t .. 8t+7, i.e. slice u = t/8, half h = (t/4)%2,
 // fields 8(t%4) .. +7 (48 bits at bit 48(t%4) of lane m%32 + 32h's six
 // dwords); lanes t and t^1 pair their 48-bit chunks and the even one writes
 // the three dwords they fill.  Tokens in [M, Mpad) get codes 0, no scale.
-__device__ __forceinline__ void act_quant_fp6_body(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-                                                   uint8_t* __restrict__ aimg, float* __restrict__ saT, int64_t Mpad,
-                                                   int64_t bx, int64_t j) {
-  const int64_t m = bx * 16 + (threadIdx.x >> 4);
-  const int t = threadIdx.x & 15;
-  if (m >= Mpad) return;  // whole 16-lane teams leave together
-  const int64_t G = K / kGroup;
+constexpr int kActGroups = 4;  // groups per act-quant team
+
+__device__ __forceinline__ void act_quant_fp6_group(const uint4 raw, int64_t m, int t, int64_t G, int64_t j,
+                                                    uint8_t* __restrict__ aimg, float* __restrict__ saT,
+                                                    int64_t Mpad) {
   float f[8];
-  if (m < M) {
-    unpack_h8(*reinterpret_cast<const uint4*>(x + m * ldx + j * kGroup + t * 8), f);
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = 0.0f;
-  }
+  unpack_h8(raw, f);
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(f[i]));
@@ -58,6 +52,25 @@ __device__ __forceinline__ void act_quant_fp6_body(const uint16_t* __restrict__ 
     }
   }
   if (t == 0) saT[j * Mpad + m] = s;  // group-major; padding rows get 0
+}
+
+__device__ __forceinline__ void act_quant_fp6_body(const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
+                                                   uint8_t* __restrict__ aimg, float* __restrict__ saT, int64_t Mpad,
+                                                   int64_t bx, int64_t jq) {
+  const int64_t m = bx * 16 + (threadIdx.x >> 4);
+  const int t = threadIdx.x & 15;
+  if (m >= Mpad) return;  // whole 16-lane teams leave together
+  const int64_t G = K / kGroup, j0 = jq * kActGroups;
+  const int nj = (int)min((int64_t)kActGroups, G - j0);  // the same for the whole workgroup
+  uint4 raw[kActGroups];
+#pragma unroll
+  for (int q = 0; q < kActGroups; ++q) {
+    raw[q] = make_uint4(0, 0, 0, 0);  // fp16 zeros: padding rows
+    if (m < M && q < nj) raw[q] = *reinterpret_cast<const uint4*>(x + m * ldx + (j0 + q) * kGroup + t * 8);
+  }
+#pragma unroll
+  for (int q = 0; q < kActGroups; ++q)
+    if (q < nj) act_quant_fp6_group(raw[q], m, t, G, j0 + q, aimg, saT, Mpad);
 }
 
 // A lane's 32 codes (four packed words) -> its two pieces of slice u.
@@ -87,10 +100,7 @@ __global__ __launch_bounds__(256) void acts_fp6_kernel(const uint8_t* __restrict
 
 // Base weight codes in the slab layout (row n, group j, codes 32c .. 32c+31
 // at qw + (n/16)*8K + j*1024 + (16c + n%16)*16) -> image.
-__device__ __forceinline__ void weights_fp6_body(const uint8_t* __restrict__ qw, int64_t K, uint8_t* __restrict__ wimg,
-                                                 int64_t total, int64_t bx) {
-  const int64_t i = bx * 256 + threadIdx.x;
-  if (i >= total) return;
+__device__ __forceinline__ uint4 weights_fp6_load(const uint8_t* __restrict__ qw, int64_t K, int64_t i) {
   const int64_t G = K / kGroup;
   const int l = (int)(i & 63);
   const int u = (int)((i >> 6) & 1);
@@ -98,8 +108,14 @@ __device__ __forceinline__ void weights_fp6_body(const uint8_t* __restrict__ qw,
   const int64_t cb = bj / G, j = bj - cb * G;
   const int64_t n = cb * 32 + (l & 31);
   const int c = 2 * u + (l >> 5);
-  const uint4 v = *reinterpret_cast<const uint4*>(qw + (n >> 4) * 8 * K + j * 1024 + (16 * c + (n & 15)) * 16);
-  put_lane(wimg + bj * kFp6Frag, u, l, v);
+  return *reinterpret_cast<const uint4*>(qw + (n >> 4) * 8 * K + j * 1024 + (16 * c + (n & 15)) * 16);
+}
+
+__device__ __forceinline__ void weights_fp6_body(const uint8_t* __restrict__ qw, int64_t K, uint8_t* __restrict__ wimg,
+                                                 int64_t total, int64_t bx) {
+  const int64_t i = bx * 256 + threadIdx.x;
+  if (i >= total) return;
+  put_lane(wimg + (i >> 7) * kFp6Frag, (int)((i >> 6) & 1), (int)(i & 63), weights_fp6_load(qw, K, i));
 }
 
 // Residual blocks (row r of block e: b/2 bytes at qr + (e*b + r)*(b/2)) ->
@@ -155,21 +171,31 @@ struct Fp6Prep {
   int64_t rtotal;
   int64_t na_x, na, nw;  // act-quant grid width (Mpad/16), act-quant blocks, base blocks
 };
+constexpr int kWeightItems = 4;  // base-image items per thread of the preparation launch
 __global__ __launch_bounds__(256) void fp6_prep_kernel(Fp6Prep p) {
   const int64_t b = blockIdx.x;
   if (b < p.na) {
     act_quant_fp6_body(p.x, p.M, p.K, p.ldx, p.aimg, p.sa, p.Mpad, b % p.na_x, b / p.na_x);
   } else if (b < p.na + p.nw) {
-    const int64_t bw = b - p.na;
-    weights_fp6_body(p.qw, p.K, p.wimg, p.wtotal, bw);
-    // the weight scales group-major: the thread of (column block cb, group j,
-    // slice 0, lane l < 32) copies sw[n][j], n = 32 cb + l
-    const int64_t i = bw * 256 + threadIdx.x;
-    const int l = (int)(i & 63);
-    if (i < p.wtotal && ((i >> 6) & 1) == 0 && l < 32) {
-      const int64_t G = p.K / kGroup, bj = i >> 7;
-      const int64_t cb = bj / G, j = bj - cb * G, n = cb * 32 + l;
-      p.swT[j * p.N + n] = p.sw[n * G + j];
+    // items bw*1024 + 256q + tid, q < 4: the four loads first
+    const int64_t i0 = (b - p.na) * (256 * kWeightItems) + threadIdx.x;
+    uint4 v[kWeightItems];
+#pragma unroll
+    for (int q = 0; q < kWeightItems; ++q)
+      if (i0 + 256 * q < p.wtotal) v[q] = weights_fp6_load(p.qw, p.K, i0 + 256 * q);
+#pragma unroll
+    for (int q = 0; q < kWeightItems; ++q) {
+      const int64_t i = i0 + 256 * q;
+      if (i >= p.wtotal) break;
+      const int l = (int)(i & 63), u = (int)((i >> 6) & 1);
+      put_lane(p.wimg + (i >> 7) * kFp6Frag, u, l, v[q]);
+      // the weight scales group-major: the thread of (column block cb,
+      // group j, slice 0, lane l < 32) copies sw[n][j], n = 32 cb + l
+      if (u == 0 && l < 32) {
+        const int64_t G = p.K / kGroup, bj = i >> 7;
+        const int64_t cb = bj / G, j = bj - cb * G, n = cb * 32 + l;
+        p.swT[j * p.N + n] = p.sw[n * G + j];
+      }
     }
   } else {
     residual_fp6_body(p.qr, p.block, p.rimg, p.rtotal, b - p.na - p.nw);
@@ -200,8 +226,8 @@ hipError_t launch_fp6_layer_prep(const uint16_t* x, int64_t M, int64_t K, int64_
   p.rimg = rimg;
   p.rtotal = n_select > 0 ? (int64_t)n_select * (block / 32) * (block / 64) * 64 : 0;
   p.na_x = p.Mpad / 16;
-  p.na = p.na_x * (K / kGroup);
-  p.nw = (p.wtotal + 255) / 256;
+  p.na = p.na_x * ((K / kGroup + kActGroups - 1) / kActGroups);
+  p.nw = (p.wtotal + 256 * kWeightItems - 1) / (256 * kWeightItems);
   const int64_t nr = (p.rtotal + 255) / 256;
   hipLaunchKernelGGL(fp6_prep_kernel, dim3((unsigned)(p.na + p.nw + nr)), dim3(256), 0, st, p);
   return hipGetLastError();
