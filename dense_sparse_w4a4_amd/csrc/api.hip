@@ -242,6 +242,15 @@ static size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 // conversion from about 1000 tokens on (measured on the Qwen3-32B MLP
 // shapes: at M = 256 the conversion costs more than it saves).
 constexpr int64_t kFp6MinM = 1024;
+// Below this many tokens mq_fused_gemm's fp6 route (taken there only when
+// the caller asks for it) reads the base codes from the packed slabs,
+// re-encoded in the kernel's registers, instead of converting them into an
+// image first: measured on the Qwen3-32B MLP shapes at 64-512 tokens it is
+// 1-2% faster than the int8 route, against about 30 us for the image
+// conversion; from 1024 tokens, where each weight tile serves four or more
+// token tiles, the in-kernel re-encoding costs more than the conversion
+// (M = 1024: 319 against 260 us).
+constexpr int64_t kFp6RawBelow = 1024;
 // (MQ_FLAG_FP6_TILE lowers it to the tile kernel's M > 32 for checks.)
 
 
@@ -293,17 +302,19 @@ static size_t gemm_workspace(int64_t M, int64_t N, int64_t K) {
 }
 
 // Points a at the fp6 images in ws (layout of fp6_images_bytes) and
-// enqueues the conversions of the weights and the residual blocks.
+// enqueues the conversions of the weights (from kFp6RawBelow tokens) and of
+// the residual blocks.
 static hipError_t fp6_prepare(GemmArgs& a, uint8_t* ws, hipStream_t st) {
   uint8_t* aimg = ws;
   uint8_t* wimg = aimg + round256(fp6_rows_bytes(a.M, a.K));
   uint8_t* rimg = wimg + round256(fp6_rows_bytes(a.N, a.K));
-  hipError_t e = launch_weights_fp6(a.qw, a.N, a.K, wimg, st);
+  const bool raw = a.M < kFp6RawBelow;
+  hipError_t e = raw ? hipSuccess : launch_weights_fp6(a.qw, a.N, a.K, wimg, st);
   if (e != hipSuccess) return e;
   e = launch_residual_fp6(a.qr, a.n_select, a.block, rimg, st);
   if (e != hipSuccess) return e;
   a.aimg = aimg;
-  a.wimg = wimg;
+  a.wimg = raw ? nullptr : wimg;
   a.rimg = rimg;
   return hipSuccess;
 }

@@ -220,7 +220,7 @@ hipError_t launch_fp6_layer_prep(const uint16_t* x, int64_t M, int64_t K, int64_
   p.N = N;
   p.wimg = wimg;
   p.swT = swT;
-  p.wtotal = N / 32 * (K / kGroup) * 128;
+  p.wtotal = wimg ? N / 32 * (K / kGroup) * 128 : 0;  // no image: the kernel reads the slabs
   p.qr = qr;
   p.block = block;
   p.rimg = rimg;

@@ -33,5 +33,6 @@ constexpr float kInv256 = 1.0f / 256.0f;
 // S_WAITCNT immediate (gfx9 family): vmcnt(4) with expcnt and lgkmcnt left
 // unconstrained (vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8).
 constexpr unsigned kWaitVm4 = 0x4u | (0x7u << 4) | (0xFu << 8);
+constexpr unsigned kWaitVm5 = 0x5u | (0x7u << 4) | (0xFu << 8);
 
 }  // namespace mq

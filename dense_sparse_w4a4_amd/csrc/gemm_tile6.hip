@@ -141,13 +141,17 @@ __device__ __forceinline__ uint32_t split_bf16(float x) {
 }
 
 struct Stage6 {
+  v4i W;  // raw base codes (weights without an image): 32 codes of one lane slice
   v4i Rlo;
   u32x2 Rhi;
   uint32_t sc;  // activation scale bits (waves 0-3) or weight scale bits (waves 4-5)
   uint32_t sr;  // residual row scale bits
 };
 
-template <int BLK, bool DUMP>
+// WRAW: no weight image; the base codes are read from the packed slab
+// layout into registers (one lane slice, 32 codes, per thread and group),
+// re-encoded there and stored to LDS like the residual pieces.
+template <int BLK, bool DUMP, bool WRAW>
 __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
   using C = Tile6Cfg<BLK>;
   extern __shared__ __align__(16) unsigned char smem[];
@@ -229,9 +233,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
   const int64_t ncb = a.N / 32;
   const uint8_t* srcA = a.aimg + min(m0 / 32 + wave, nrb - 1) * G * kFp6Frag + lane * 16;
   const int pB0 = wave, pB1 = wave + 8;
-  const uint8_t* srcB0 = a.wimg + min(n0 / 32 + pB0 / 3, ncb - 1) * G * kFp6Frag + (pB0 % 3) * 1024 + lane * 16;
+  const uint8_t* wimg = WRAW ? a.qw : a.wimg;  // (no image: B pointers unused)
+  const uint8_t* srcB0 = wimg + min(n0 / 32 + pB0 / 3, ncb - 1) * G * kFp6Frag + (pB0 % 3) * 1024 + lane * 16;
   const uint8_t* srcB1 =
-      a.wimg + min(n0 / 32 + (pB1 < 12 ? pB1 : 0) / 3, ncb - 1) * G * kFp6Frag + (pB1 % 3) * 1024 + lane * 16;
+      wimg + min(n0 / 32 + (pB1 < 12 ? pB1 : 0) / 3, ncb - 1) * G * kFp6Frag + (pB1 % 3) * 1024 + lane * 16;
   const uint32_t dstB0 = (uint32_t)(C::B_OFF + (pB0 / 3) * kFp6Frag + (pB0 % 3) * 1024);
   const uint32_t dstB1 = (uint32_t)(C::B_OFF + ((pB1 < 12 ? pB1 : 0) / 3) * kFp6Frag + (pB1 % 3) * 1024);
   typedef __attribute__((address_space(3))) void* lds_ptr;
@@ -243,16 +248,27 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
       __builtin_amdgcn_global_load_lds(srcA + jo + p * 1024,
                                        (lds_ptr)(uintptr_t)(st + C::A_OFF + (uint32_t)wave * kFp6Frag + p * 1024), 16,
                                        0, 0);
-    __builtin_amdgcn_global_load_lds(srcB0 + jo, (lds_ptr)(uintptr_t)(st + dstB0), 16, 0, 0);
-    if (wave < 4) __builtin_amdgcn_global_load_lds(srcB1 + jo, (lds_ptr)(uintptr_t)(st + dstB1), 16, 0, 0);
+    if (!WRAW) {
+      __builtin_amdgcn_global_load_lds(srcB0 + jo, (lds_ptr)(uintptr_t)(st + dstB0), 16, 0, 0);
+      if (wave < 4) __builtin_amdgcn_global_load_lds(srcB1 + jo, (lds_ptr)(uintptr_t)(st + dstB1), 16, 0, 0);
+    }
   };
+  // raw base codes: thread tid makes lane lw = tid % 64 of slice uw6 =
+  // (tid / 64) % 2 of the tile's column block cw = tid / 128 (past N: the
+  // last one), codes 32c .. 32c+31 of row n, c = 2 uw6 + lw / 32, at
+  // qw + (n/16)*8K + j*1024 + (16c + n%16)*16 in the slab layout
+  const int cw = tid >> 7, uw6 = (tid >> 6) & 1, lw = tid & 63;
+  const int64_t nw = min(n0 / 32 + cw, ncb - 1) * 32 + (lw & 31);
+  const uint8_t* srcW = a.qw + (nw >> 4) * 8 * a.K + (16 * (2 * uw6 + (lw >> 5)) + (nw & 15)) * 16;
+  const uint32_t dstWlo = (uint32_t)(C::B_OFF + cw * kFp6Frag + fp6_lo_offset(uw6, lw));
+  const uint32_t dstWhi = (uint32_t)(C::B_OFF + cw * kFp6Frag + fp6_hi_offset(uw6, lw));
   // after a step's loads: the step's DMA (issued before the step's four
   // register loads: scale, residual pieces, residual scale) has completed.
   // The builtin (vmcnt 4; expcnt, lgkmcnt unconstrained) rather than inline
   // asm, so that the compiler's own wait analysis knows every older load is
   // done and adds no vmcnt(0) before the next step's stores.
   auto dma_wait = [&]() {
-    __builtin_amdgcn_s_waitcnt(kWaitVm4);
+    __builtin_amdgcn_s_waitcnt(WRAW ? kWaitVm5 : kWaitVm4);  // WRAW: five register loads a step
     asm volatile("" ::: "memory");
   };
 
@@ -296,6 +312,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
 
   auto load = [&](Stage6& S, int j) {
     j = min(j, je - 1);
+    if (WRAW) S.W = *reinterpret_cast<const v4i*>(srcW + (int64_t)j * 1024);
     if (wave < 4) {
       S.sc = *reinterpret_cast<const uint32_t*>(scb + j * sc_step);
     } else {
@@ -313,6 +330,18 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile6_kernel(GemmArgs a) {
   };
 
   auto store = [&](uint32_t st, const Stage6& S, int j) {
+    if (WRAW) {
+      const uint32_t w[4] = {(uint32_t)S.W[0], (uint32_t)S.W[1], (uint32_t)S.W[2], (uint32_t)S.W[3]};
+      uint32_t d[6];
+      fp6_fields32(w, d);
+      v4i lo;
+      lo[0] = (int)d[0];
+      lo[1] = (int)d[1];
+      lo[2] = (int)d[2];
+      lo[3] = (int)d[3];
+      lds_st16(st + dstWlo, lo);
+      lds_st8(st + dstWhi, d[4], d[5]);
+    }
     if (wave < 4) {
       // activation scale * 64 (the fields' 1/8 on both operands): (hi, lo, hi, lo)
       const float s = (m0 + tid < a.M) ? __uint_as_float(S.sc) * 64.0f : 0.f;
@@ -525,11 +554,11 @@ __global__ __launch_bounds__(256) void split_reduce6_kernel(const float* __restr
   *reinterpret_cast<uint2*>(y + m * ldy + n) = make_uint2(lo, hi);
 }
 
-template <int BLK, bool DUMP>
+template <int BLK, bool DUMP, bool WRAW>
 hipError_t launch_tile6_cfg(const GemmArgs& a, hipStream_t st) {
   using C = Tile6Cfg<BLK>;
   const size_t lds = C::lds(a.K);
-  auto kern = gemm_tile6_kernel<BLK, DUMP>;
+  auto kern = gemm_tile6_kernel<BLK, DUMP, WRAW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -626,8 +655,12 @@ bool tile6_gemm_fits(const GemmArgs& a) {
 
 hipError_t launch_tile6_gemm(const GemmArgs& a, hipStream_t st) {
   const bool d = a.acc_dump != nullptr;
-  if (a.block == 64) return d ? launch_tile6_cfg<64, true>(a, st) : launch_tile6_cfg<64, false>(a, st);
-  return d ? launch_tile6_cfg<128, true>(a, st) : launch_tile6_cfg<128, false>(a, st);
+  if (a.wimg == nullptr) {  // base codes from the packed slabs
+    if (a.block == 64) return d ? launch_tile6_cfg<64, true, true>(a, st) : launch_tile6_cfg<64, false, true>(a, st);
+    return d ? launch_tile6_cfg<128, true, true>(a, st) : launch_tile6_cfg<128, false, true>(a, st);
+  }
+  if (a.block == 64) return d ? launch_tile6_cfg<64, true, false>(a, st) : launch_tile6_cfg<64, false, false>(a, st);
+  return d ? launch_tile6_cfg<128, true, false>(a, st) : launch_tile6_cfg<128, false, false>(a, st);
 }
 
 }  // namespace mq

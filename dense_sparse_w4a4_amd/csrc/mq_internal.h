@@ -252,9 +252,10 @@ struct GemmArgs {
                       // (packed qa, widened while staged)
   const uint8_t* qat; // streaming kernel: packed activation codes in 16-token
                       // tiles (tiled_a_index), or null (qa row-major)
-  // fp6 route of the tile kernel (all three set, or none): FP6 images of the
-  // activation codes [ceil(M/32)][K/128][3 KB], the base weight codes
-  // [N/32][K/128][3 KB] and the residual blocks [n_select][b*b*3/4]
+  // fp6 route of the tile kernel (aimg and rimg set, or none): FP6 images of
+  // the activation codes [ceil(M/32)][K/128][3 KB], the base weight codes
+  // [N/32][K/128][3 KB] (or null: the kernel reads the packed slabs qw) and
+  // the residual blocks [n_select][b*b*3/4]
   const uint8_t* aimg;
   const uint8_t* wimg;
   const uint8_t* rimg;
@@ -316,7 +317,8 @@ hipError_t launch_weights_fp6(const uint8_t* qw, int64_t N, int64_t K, uint8_t* 
 hipError_t launch_residual_fp6(const uint8_t* qr, int n_select, int block, uint8_t* rimg, hipStream_t st);
 // act-quant into the activation image, base and residual conversion, in one launch
 // (the activation scales written group-major, saT [K/128][wide_rows(M)];
-// the weight scales sw [N][K/128] copied group-major into swT [K/128][N])
+// the weight scales sw [N][K/128] copied group-major into swT [K/128][N];
+// wimg null: no base conversion and no swT copy)
 hipError_t launch_fp6_layer_prep(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* aimg, float* saT,
                                  const uint8_t* qw, const uint16_t* sw, int64_t N, uint8_t* wimg, uint16_t* swT,
                                  const uint8_t* qr, int n_select, int block, uint8_t* rimg, hipStream_t st);

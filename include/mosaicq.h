@@ -206,7 +206,9 @@ mq_status mq_select_exact_greedy(const uint16_t* w, const uint16_t* x_calib, int
 /* mq_fused_gemm flags choosing the prefill kernel's route (measurement and
  * cross-checks; both give the same y bits): the int8 route even where the
  * fp6 route would run, or the fp6 route already from M = 33 (by default
- * from M = 1024) when the workspace holds its images and block is 64 or 128. */
+ * from M = 1024) when the workspace holds its images and block is 64 or 128.
+ * Below M = 1024 that route converts no weight image: the kernel re-encodes
+ * the packed base codes as it stages them. */
 #define MQ_FLAG_INT8_TILE 2u
 #define MQ_FLAG_FP6_TILE 4u
 

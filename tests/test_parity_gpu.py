@@ -195,7 +195,9 @@ def test_fused_gemm_accumulators_exact_and_y(M, N, K, b, rho):
                                          (1030, 256, 1024, 64, 0.10)])
 def test_fp6_route_matches_int8_route(M, N, K, b, rho):
     # the prefill kernel's two routes on the same codes: identical exact
-    # accumulators and identical y bits, with and without the dump
+    # accumulators (the oracle's) and identical y bits, with and without the
+    # dump; below 1024 tokens the fp6 route re-encodes the packed base codes
+    # in the kernel, from 1024 it converts them into an image first
     print(f"fp6 vs int8 M={M} N={N} K={K} b={b} rho={rho}", flush=True)
     spec = syn.LayerSpec("r", K=K, N=N, w_outlier_frac=0.01, x_outlier_count=3,
                          T=32, block=b, rho=rho)
@@ -213,6 +215,11 @@ def test_fp6_route_matches_int8_route(M, N, K, b, rho):
     z8 = ops.fused_gemm(qa, sa, layer, route="int8")
     torch.cuda.synchronize()
     assert torch.equal(a6, a8) and torch.equal(r6, r8)
+    y_ref, acc_ref, res_ref = oracle.fused_gemm(rqa, rsa, ref)
+    assert np.array_equal(host(a6).astype(np.int64), acc_ref)
+    if len(res_ref):
+        assert np.array_equal(host(r6).astype(np.int64), np.stack(res_ref))
+    assert_y_close(y6, y_ref)
     assert np.array_equal(host(y6).view(np.uint16), host(y8).view(np.uint16))
     assert np.array_equal(host(z6).view(np.uint16), host(z8).view(np.uint16))
     assert np.array_equal(host(z6).view(np.uint16), host(y6).view(np.uint16))
