@@ -525,19 +525,35 @@ __global__ __launch_bounds__(NTHR, 1) void gemm_tile_kernel(GemmArgs a) {
   if (j < je) compute(st0, j);  // odd group count: the last group
 
   // ---- output ----
+  // fp16 output in 4-byte stores: lanes 2i and 2i+1 hold channels n and n+1
+  // of the same rows, and of each row pair (e, e+1) they swap one value (a
+  // DPP move within lane pairs), so the even lane writes row e at (n, n+1)
+  // and the odd lane row e+1 at (n-1, n).  Every such store is aligned (y
+  // 16-byte aligned, ldy a multiple of 8) and n < N implies n+1 < N (N is a
+  // multiple of the block edge, so of 32).
+  const bool odd = lane & 1;
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
     for (int cb = 0; cb < 2; ++cb) {
       const int64_t n = n0 + (wn * 2 + cb) * 32 + (lane & 31);
+      if (a.part) {
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int64_t m = m0 + (wm * 2 + rb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        if (m < a.M && n < a.N) {
-          if (a.part)
-            a.part[((int64_t)split * a.M + m) * a.N + n] = y[rb][cb][e];
-          else
-            a.y[m * a.ldy + n] = f2h_bits(y[rb][cb][e]);
+        for (int e = 0; e < 16; ++e) {
+          const int64_t m = m0 + (wm * 2 + rb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+          if (m < a.M && n < a.N) a.part[((int64_t)split * a.M + m) * a.N + n] = y[rb][cb][e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+          const float v0 = y[rb][cb][e], v1 = y[rb][cb][e + 1];
+          // quad_perm (1, 0, 3, 2): each lane reads its pair partner
+          const float r = __int_as_float(
+              __builtin_amdgcn_update_dpp(0, __float_as_int(odd ? v0 : v1), 0xB1, 0xF, 0xF, false));
+          const int64_t m = m0 + (wm * 2 + rb) * 32 + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3) + (odd ? 1 : 0);
+          const uint32_t lo = f2h_bits(odd ? r : v0), hi = f2h_bits(odd ? v1 : r);
+          if (m < a.M && n < a.N)
+            *reinterpret_cast<uint32_t*>(a.y + m * a.ldy + (n & ~(int64_t)1)) = lo | (hi << 16);
         }
       }
     }
